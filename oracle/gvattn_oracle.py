@@ -1,0 +1,233 @@
+"""FP64 CPU oracle for segmented ("gapped") varlen attention and its LSE merge.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, obviously correct
+definition that the HIP path is checked against.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it; the product package never does, and the two share no code.
+
+What it computes (the sources are the pages' own statements of the method):
+
+* cosmos-framework PR #302, "What": every segment has a row capacity and a
+  used prefix (seqused_q / seqused_k); the used query rows of a segment attend
+  the used keys/values of the same segment only; rows past a segment's used
+  length are left as they are; a segment with no keys gets a zero output and
+  a -inf log-sum-exp.  PR #302, "Tests": the forward is checked against a
+  per-segment FP64 reference -- this module is that reference.
+* TensorRT-LLM issue #18687, "actual behavior" and "additional notes": keys
+  past the used length must be masked, not merely zero, because a zero key
+  has logit 0 and would add exp(0) = 1 to the softmax denominator.
+* cosmos-framework PR #312, "Problem and behavior": GQA folding (several query
+  heads share one KV head) and an FP32 LSE merge of the partial results of
+  visibility partitions.
+
+Readings taken where the pages leave a step open:
+
+* query head h uses KV head ``h // (Hq // Hkv)`` (GQA folding, groups of
+  consecutive heads);
+* causal masks are aligned bottom-right inside each segment: row i (0-based
+  in the segment) sees key j iff ``j <= i + used_k - used_q``;
+* a row with no visible key (an empty segment, or a causal row above the
+  diagonal when used_k < used_q) gets O = +0 and LSE = -inf;
+* LSE is the natural log of sum_j exp(scale * q.k_j), scale included;
+* layouts: Q [Tq, Hq, D], K [Tk, Hkv, D], V [Tk, Hkv, Dv], O [Tq, Hq, Dv],
+  LSE [Hq, Tq] (the [H, total_q] layout named in the PR #302 review);
+* the merge works on used rows only and leaves gap rows untouched.
+
+Everything is computed in float64 from the exact input values (float32 arrays
+whose values are bf16-exact for bf16 workloads; ``scale`` is the float32 value
+the kernel uses, widened).
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import os
+
+import numpy as np
+
+try:  # BLAS threads would oversubscribe the worker pool
+    from threadpoolctl import threadpool_limits as _threadpool_limits
+except Exception:  # pragma: no cover
+    _threadpool_limits = None
+
+# Row-block byte budget for the [rows, used_k] float64 score block.  The
+# block's row count is max(1, budget // (used_k * 8)), the sizing rule the
+# PR #302 review asks of the FP32 per-segment matmul path.
+SCORE_BUDGET_BYTES = 64 << 20
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def visible_limit(i: np.ndarray, uq: int, uk: int, causal: bool) -> np.ndarray:
+    """Number of keys row i of a segment may see (bottom-right causal)."""
+    i = np.asarray(i, dtype=np.int64)
+    if not causal:
+        return np.full(i.shape, uk, dtype=np.int64)
+    return np.clip(i + uk - uq + 1, 0, uk)
+
+
+def segment_head_rows(q, k, v, q0: int, k0: int, uq: int, uk: int, h: int,
+                      hkv_of_h: int, scale: float, causal: bool,
+                      rows: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Attention of the given segment rows (indices in [0, uq)) for one query
+    head.  Returns (O [n, Dv] float64, LSE [n] float64)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    dv = v.shape[2]
+    n = rows.shape[0]
+    o = np.zeros((n, dv), dtype=np.float64)
+    lse = np.full(n, -np.inf, dtype=np.float64)
+    if n == 0 or uk == 0:
+        return o, lse
+    qs = np.asarray(q[q0 + rows, h, :], dtype=np.float64)            # [n, D]
+    ks = np.asarray(k[k0:k0 + uk, hkv_of_h, :], dtype=np.float64)    # [uk, D]
+    vs = np.asarray(v[k0:k0 + uk, hkv_of_h, :], dtype=np.float64)    # [uk, Dv]
+    s = float(scale) * (qs @ ks.T)                                   # [n, uk]
+    if causal:
+        lim = visible_limit(rows, uq, uk, True)                      # [n]
+        cols = np.arange(uk, dtype=np.int64)
+        s = np.where(cols[None, :] < lim[:, None], s, -np.inf)
+    m = s.max(axis=1)                                                # [n]
+    live = m > -np.inf
+    if not live.any():
+        return o, lse
+    sl, ml = s[live], m[live]
+    p = np.exp(sl - ml[:, None])
+    l = p.sum(axis=1)
+    o[live] = (p @ vs) / l[:, None]
+    lse[live] = ml + np.log(l)
+    # NaN inputs inside the used rows propagate (max ignores nothing here).
+    nan_rows = np.isnan(m)
+    if nan_rows.any():
+        o[nan_rows] = np.nan
+        lse[nan_rows] = np.nan
+    return o, lse
+
+
+def _work_items(cu_q, cu_k, used_q, used_k, hq, hkv):
+    g = hq // hkv
+    for s in range(len(used_q)):
+        uq, uk = int(used_q[s]), int(used_k[s])
+        if uq == 0:
+            continue
+        for h in range(hq):
+            yield s, h, h // g, int(cu_q[s]), int(cu_k[s]), uq, uk
+
+
+def attention_fwd(q, k, v, cu_q, cu_k, used_q, used_k, scale, causal,
+                  out_init=None, lse_init=None, workers: int | None = None,
+                  segments=None):
+    """Whole-launch oracle.  Returns (O [Tq, Hq, Dv] float64,
+    LSE [Hq, Tq] float64); rows not written keep ``out_init``/``lse_init``
+    (zeros when not given).  ``segments`` restricts the work to a subset of
+    segments (their rows only are written)."""
+    tq, hq, _ = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    if hq % hkv:
+        raise ValueError(f"hq={hq} is not a multiple of hkv={hkv}")
+    out = (np.zeros((tq, hq, dv)) if out_init is None
+           else np.array(out_init, dtype=np.float64, copy=True))
+    lse = (np.zeros((hq, tq)) if lse_init is None
+           else np.array(lse_init, dtype=np.float64, copy=True))
+    items = list(_work_items(cu_q, cu_k, used_q, used_k, hq, hkv))
+    if segments is not None:
+        keep = set(int(s) for s in segments)
+        items = [it for it in items if it[0] in keep]
+
+    def run(item):
+        s, h, g, q0, k0, uq, uk = item
+        step = max(1, SCORE_BUDGET_BYTES // (max(uk, 1) * 8))
+        for r0 in range(0, uq, step):
+            rows = np.arange(r0, min(uq, r0 + step))
+            o, l = segment_head_rows(q, k, v, q0, k0, uq, uk, h, g, scale,
+                                     causal, rows)
+            out[q0 + rows, h, :] = o
+            lse[h, q0 + rows] = l
+
+    workers = workers or host_cores()
+    if workers <= 1 or len(items) <= 1:
+        for it in items:
+            run(it)
+    else:
+        ctx = (_threadpool_limits(limits=1) if _threadpool_limits is not None
+               else _NullCtx())
+        with ctx, _cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(run, items))
+    return out, lse
+
+
+class _NullCtx:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+def lse_merge(part_out, part_lse, cu_q, used_q, out_init=None, lse_init=None):
+    """Merge the (O_p, LSE_p) partials of several key partitions, row by row
+    and head by head, in float64 (cosmos-framework PR #312, "Problem and
+    behavior": visibility partitions combined by an FP32 LSE merge).
+
+    For each used row and head: m = max_p LSE_p; if m = -inf the result is
+    O = 0, LSE = -inf; otherwise w_p = exp(LSE_p - m), W = sum_p w_p,
+    LSE = m + ln W and O = sum_p (w_p / W) O_p.  Gap rows keep the initial
+    values."""
+    tq, hq, dv = part_out[0].shape
+    out = (np.zeros((tq, hq, dv)) if out_init is None
+           else np.array(out_init, dtype=np.float64, copy=True))
+    lse = (np.zeros((hq, tq)) if lse_init is None
+           else np.array(lse_init, dtype=np.float64, copy=True))
+    for s in range(len(used_q)):
+        q0, uq = int(cu_q[s]), int(used_q[s])
+        if uq == 0:
+            continue
+        rows = slice(q0, q0 + uq)
+        L = np.stack([np.asarray(pl[:, rows], np.float64) for pl in part_lse])  # [P, Hq, uq]
+        O = np.stack([np.asarray(po[rows], np.float64) for po in part_out])     # [P, uq, Hq, Dv]
+        m = L.max(axis=0)                                                        # [Hq, uq]
+        dead = m == -np.inf
+        m_safe = np.where(dead, 0.0, m)
+        w = np.exp(L - m_safe[None])                                             # [P, Hq, uq]
+        W = w.sum(axis=0)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            merged_lse = np.where(dead, -np.inf, m_safe + np.log(W))
+            frac = np.where(dead[None], 0.0, w / W[None])                        # [P, Hq, uq]
+        frac_t = np.transpose(frac, (0, 2, 1))[..., None]                        # [P, uq, Hq, 1]
+        merged = (frac_t * O).sum(axis=0)
+        merged[np.transpose(dead)] = 0.0
+        out[rows] = merged
+        lse[:, rows] = merged_lse
+    return out, lse
+
+
+def attention_flops(used_q, used_k, hq: int, d: int, dv: int, causal: bool) -> int:
+    """Algorithmic FLOPs of one forward over used rows: every visible
+    (query, key) pair costs 2*d (scores) + 2*dv (P.V) per query head."""
+    pairs = 0
+    for uq, uk in zip(used_q, used_k):
+        uq, uk = int(uq), int(uk)
+        if uq == 0 or uk == 0:
+            continue
+        if not causal:
+            pairs += uq * uk
+        else:
+            pairs += int(visible_limit(np.arange(uq), uq, uk, True).sum())
+    return pairs * hq * (2 * d + 2 * dv)
+
+
+def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
+    """Bitwise equality of two float32 arrays (used for gap-row checks)."""
+    a = np.ascontiguousarray(a, np.float32).view(np.uint32)
+    b = np.ascontiguousarray(b, np.float32).view(np.uint32)
+    return bool(np.array_equal(a, b))
+
+
+__all__ = [
+    "attention_fwd", "lse_merge", "segment_head_rows", "visible_limit",
+    "attention_flops", "host_cores", "bits_equal", "SCORE_BUDGET_BYTES",
+]

@@ -1,0 +1,415 @@
+"""Pins for the FP64 oracle, checked against things other than itself.
+
+Each test targets a mistake the oracle could plausibly make (a dropped mask,
+a wrong causal offset, a wrong GQA head mapping, a transposed operand, a
+missing log, a broken merge weight).  Sources: brute force on tiny inputs,
+closed forms, torch's own scaled_dot_product_attention / logsumexp as a
+library routine, and the invariants the pages state (tests/golden).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from segmented_varlen_attention_amd import workloads as W
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def run_oracle(wl, geom=None, out_init=None, lse_init=None, workers=2):
+    g = geom or wl.geom
+    return oracle.attention_fwd(
+        wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k, float(g.scale),
+        g.causal,
+        wl.out_init() if out_init is None else out_init,
+        wl.lse_init() if lse_init is None else lse_init, workers=workers)
+
+
+# --- brute force ------------------------------------------------------------
+
+def brute_force(q, k, v, cu_q, cu_k, used_q, used_k, scale, causal, sentinel):
+    """Scalar loops over global rows; no slicing, no max subtraction, exact
+    sums (math.fsum).  Visibility is decided key by key: key j of the row's
+    segment is visible when j < used_k and, under causal, when the key's
+    distance from the end of the used keys is at least the row's distance
+    from the end of the used queries."""
+    tq, hq, _ = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    group = hq // hkv
+    out = np.full((tq, hq, dv), sentinel)
+    lse = np.full((hq, tq), sentinel)
+    nseg = len(used_q)
+    for r in range(tq):
+        s = next(i for i in range(nseg) if cu_q[i] <= r < cu_q[i + 1])
+        i = r - cu_q[s]
+        if i >= used_q[s]:
+            continue
+        for h in range(hq):
+            kvh = h // group
+            logits, vals = [], []
+            for j in range(used_k[s]):
+                if causal and (used_k[s] - 1 - j) < (used_q[s] - 1 - i):
+                    continue
+                kr = cu_k[s] + j
+                logits.append(scale * math.fsum(float(q[r, h, t]) * float(k[kr, kvh, t])
+                                                for t in range(q.shape[2])))
+                vals.append([float(x) for x in v[kr, kvh, :]])
+            if not logits:
+                out[r, h, :] = 0.0
+                lse[h, r] = -math.inf
+                continue
+            w = [math.exp(x) for x in logits]
+            total = math.fsum(w)
+            lse[h, r] = math.log(total)
+            for c in range(dv):
+                out[r, h, c] = math.fsum(w[j] * vals[j][c] for j in range(len(w))) / total
+    return out, lse
+
+
+@pytest.mark.parametrize("seed,nseg,hq,hkv,d,causal", [
+    (11, 3, 2, 2, 4, False),
+    (12, 4, 4, 2, 8, True),
+    (13, 2, 3, 1, 5, True),
+    (14, 3, 6, 2, 3, False),
+    (15, 4, 2, 1, 8, True),
+])
+def test_brute_force_tiny(seed, nseg, hq, hkv, d, causal):
+    rng = np.random.default_rng(seed)
+    caps_q = rng.integers(1, 8, size=nseg)
+    caps_k = rng.integers(1, 8, size=nseg)
+    uq = np.array([rng.integers(0, c + 1) for c in caps_q])
+    uk = np.array([rng.integers(0, c + 1) for c in caps_k])
+    uk[0] = 0                      # an empty segment
+    uq[-1] = caps_q[-1]            # a full one
+    g = W.make_geometry(caps_q, caps_k, uq, uk, hq, hkv, d, causal, dtype=W.FP32)
+    q = rng.standard_normal((g.total_q, hq, d)).astype(np.float32)
+    k = rng.standard_normal((g.total_k, hkv, d)).astype(np.float32)
+    v = rng.standard_normal((g.total_k, hkv, d)).astype(np.float32)
+    scale = 0.37
+    o_ref, l_ref = brute_force(q, k, v, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                               scale, causal, W.SENTINEL)
+    o, l = oracle.attention_fwd(q, k, v, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                                scale, causal, np.full_like(o_ref, W.SENTINEL),
+                                np.full_like(l_ref, W.SENTINEL), workers=1)
+    assert np.array_equal(np.isinf(l), np.isinf(l_ref))
+    fin = np.isfinite(l_ref)
+    assert np.max(np.abs(l[fin] - l_ref[fin]), initial=0) <= 1e-12
+    assert np.max(np.abs(o - o_ref)) <= 1e-12
+
+
+# --- closed forms -------------------------------------------------------------
+
+def test_hand_example_closed_form(golden):
+    """Two query rows, two real keys and one zero pad slot (d = 2, scale 1).
+    Row 0 scores (1, 0); row 1 scores (0, 2)."""
+    e = math.e
+    q = np.array([[[1.0, 0.0]], [[0.0, 2.0]]], np.float32)
+    k = np.array([[[1.0, 0.0]], [[0.0, 1.0]], [[0.0, 0.0]]], np.float32)
+    v = np.array([[[1.0, 2.0]], [[3.0, 4.0]], [[0.0, 0.0]]], np.float32)
+    cu_q, cu_k = np.array([0, 2]), np.array([0, 3])
+    o, l = oracle.attention_fwd(q, k, v, cu_q, cu_k, [2], [2], 1.0, False, workers=1)
+    exp_o0 = (e * np.array([1, 2]) + np.array([3, 4])) / (e + 1)
+    exp_o1 = (np.array([1, 2]) + e ** 2 * np.array([3, 4])) / (1 + e ** 2)
+    assert np.allclose(o[0, 0], exp_o0, atol=1e-14, rtol=0)
+    assert np.allclose(o[1, 0], exp_o1, atol=1e-14, rtol=0)
+    assert abs(l[0, 0] - math.log(e + 1)) < 1e-14
+    assert abs(l[0, 1] - math.log(1 + e ** 2)) < 1e-14
+    # Unmasked pad slot: it adds exp(0) = 1 to the denominator (issue #18687).
+    inc = golden["zero_key_adds_one"]["denominator_increment_per_zero_slot"]
+    o_b, l_b = oracle.attention_fwd(q, k, v, cu_q, cu_k, [2], [3], 1.0, False, workers=1)
+    assert abs(l_b[0, 0] - math.log(e + 1 + inc)) < 1e-14
+    assert np.allclose(o_b[0, 0], (e * np.array([1, 2]) + np.array([3, 4])) / (e + 1 + inc),
+                       atol=1e-14, rtol=0)
+
+
+def test_single_key_is_exact():
+    """One visible key: O = v_0 and LSE = scale * q . k_0."""
+    wl = W.random_small(21, nseg=3, cap_q=9, cap_k=5, hq=4, hkv=2, d=16,
+                        causal=False, dtype=W.FP32, lengths=([9, 4, 1], [1, 1, 1]))
+    o, l = run_oracle(wl)
+    g = wl.geom
+    for s in range(3):
+        for i in range(int(g.used_q[s])):
+            r = g.cu_q[s] + i
+            for h in range(g.hq):
+                kv = h // (g.hq // g.hkv)
+                kr = g.cu_k[s]
+                assert np.array_equal(o[r, h], wl.v[kr, kv].astype(np.float64))
+                want = float(g.scale) * float(np.dot(wl.q[r, h].astype(np.float64),
+                                                     wl.k[kr, kv].astype(np.float64)))
+                assert abs(l[h, r] - want) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_mean_and_count(causal):
+    """scale = 0: every visible key has weight 1, so O is the mean of the
+    visible V rows and LSE = ln(number of visible keys).  Under causal the
+    count of row i (bottom-right) is clamp(i + uk - uq + 1, 0, uk)."""
+    lengths = ([7, 3, 5, 6], [4, 8, 5, 0])
+    wl = W.random_small(22, nseg=4, cap_q=8, cap_k=8, hq=2, hkv=1, d=4,
+                        causal=causal, dtype=W.FP32, lengths=lengths)
+    g = wl.geom
+    o, l = oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q,
+                                g.used_k, 0.0, causal, workers=1)
+    for s in range(4):
+        uq, uk = lengths[0][s], lengths[1][s]
+        for i in range(uq):
+            n = min(uk, max(0, i + uk - uq + 1)) if causal else uk
+            r = g.cu_q[s] + i
+            if n == 0:
+                assert l[0, r] == -math.inf and np.all(o[r] == 0.0)
+                continue
+            assert abs(l[0, r] - math.log(n)) < 1e-13
+            # the visible keys are the first n of the segment
+            mean = wl.v[g.cu_k[s]:g.cu_k[s] + n, 0].astype(np.float64).mean(axis=0)
+            assert np.allclose(o[r, 0], mean, atol=1e-13, rtol=0)
+
+
+# --- library routine: torch SDPA (CPU, float64) -------------------------------
+
+def _sdpa(q, k, v, scale, causal=False, mask=None):
+    """q [n, Hq, D], k/v [m, Hkv, D] -> torch SDPA (GQA) and logsumexp."""
+    tq = torch.from_numpy(np.asarray(q, np.float64)).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(np.asarray(k, np.float64)).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(np.asarray(v, np.float64)).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, is_causal=causal,
+                                       scale=scale, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def test_sdpa_noncausal_gqa_single_segment():
+    wl = W.random_small(31, nseg=1, cap_q=37, cap_k=53, hq=6, hkv=2, d=16,
+                        causal=False, dtype=W.FP32, lengths=([37], [53]))
+    g = wl.geom
+    o, l = run_oracle(wl)
+    ref = _sdpa(wl.q, wl.k, wl.v, float(g.scale))
+    assert np.max(np.abs(o - ref)) < 1e-12
+    # LSE via torch.logsumexp of the explicit scores (GQA by repeat_interleave)
+    kq = torch.from_numpy(wl.k.astype(np.float64)).repeat_interleave(3, dim=1)
+    sc = torch.einsum("qhd,khd->hqk", torch.from_numpy(wl.q.astype(np.float64)), kq)
+    want = torch.logsumexp(float(g.scale) * sc, dim=-1).numpy()
+    assert np.max(np.abs(l - want)) < 1e-12
+
+
+@pytest.mark.parametrize("uq,uk", [(5, 19), (19, 19), (23, 9), (1, 7), (7, 1)])
+def test_sdpa_causal_bottom_right(uq, uk):
+    """Bottom-right causal equals the last rows of a square causal problem:
+    pad the queries in front to uk rows, run SDPA(is_causal=True) (top-left
+    and bottom-right coincide on a square), keep the last uq rows.  When
+    uq > uk the first uq - uk rows see no key (O = 0, LSE = -inf)."""
+    wl = W.random_small(32, nseg=1, cap_q=uq, cap_k=uk, hq=4, hkv=2, d=8,
+                        causal=True, dtype=W.FP32, lengths=([uq], [uk]))
+    g = wl.geom
+    o, l = run_oracle(wl)
+    sc = float(g.scale)
+    if uq <= uk:
+        padq = np.concatenate([np.zeros((uk - uq, 4, 8), np.float32), wl.q], axis=0)
+        ref = _sdpa(padq, wl.k, wl.v, sc, causal=True)[uk - uq:]
+        assert np.max(np.abs(o - ref)) < 1e-12
+    else:
+        dead = uq - uk
+        assert np.all(o[:dead] == 0.0) and np.all(l[:, :dead] == -np.inf)
+        ref = _sdpa(wl.q[dead:], wl.k, wl.v, sc, causal=True)
+        assert np.max(np.abs(o[dead:] - ref)) < 1e-12
+
+
+def test_sdpa_key_padding_mask():
+    """seqused_k equals a boolean key-padding mask handed to SDPA."""
+    wl = W.random_small(33, nseg=1, cap_q=16, cap_k=40, hq=4, hkv=4, d=8,
+                        causal=False, dtype=W.FP32, lengths=([16], [27]))
+    g = wl.geom
+    o, _ = run_oracle(wl)
+    mask = torch.zeros(1, 1, 16, 40, dtype=torch.bool)
+    mask[..., :27] = True
+    ref = _sdpa(wl.q, wl.k, wl.v, float(g.scale), mask=mask)
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+# --- invariants the pages state -----------------------------------------------
+
+def _padded_text_workload(seed, lens, cap, hq=4, hkv=2, d=16, nq=12):
+    g = W.make_geometry([nq] * len(lens), [cap] * len(lens), [nq] * len(lens),
+                        lens, hq, hkv, d, causal=False, dtype=W.BF16)
+    q, k, v = W.fill_qkv(g, seed)
+    for s, L in enumerate(lens):
+        k[g.cu_k[s] + L:g.cu_k[s + 1]] = 0.0
+        v[g.cu_k[s] + L:g.cu_k[s + 1]] = 0.0
+    return W.Workload("pad", seed, g, q, k, v)
+
+
+def test_trimmed_equals_masked(golden):
+    """Right-padded text under seqused_k == text trimmed per sample
+    (issue #18687: the single-GPU trim path is exact)."""
+    assert golden["trimmed_equals_masked"]
+    lens, cap = [3, 29], 32
+    wl = _padded_text_workload(41, lens, cap)
+    g = wl.geom
+    o, l = run_oracle(wl)
+    # trimmed: keep only the real keys, repacked
+    keep = np.concatenate([np.arange(g.cu_k[s], g.cu_k[s] + L) for s, L in enumerate(lens)])
+    kt, vt = wl.k[keep], wl.v[keep]
+    cu_t = np.array([0, lens[0], lens[0] + lens[1]])
+    o2, l2 = oracle.attention_fwd(wl.q, kt, vt, g.cu_q, cu_t, g.used_q, lens,
+                                  float(g.scale), False, workers=1)
+    assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(l - l2)) < 1e-12
+
+
+def test_unmasked_zero_pads_closed_form(golden):
+    """Attending the zero pad slots without a mask (the bug of issue #18687):
+    each of n_pad zero keys adds exp(0)=1 to the denominator, so
+    LSE_bug = ln(exp(LSE) + n_pad) and O_bug = O * exp(LSE) / (exp(LSE) + n_pad)."""
+    inc = golden["zero_key_adds_one"]["denominator_increment_per_zero_slot"]
+    lens, cap = [3, 29], 32
+    wl = _padded_text_workload(42, lens, cap)
+    g = wl.geom
+    o, l = run_oracle(wl)
+    gb = g.with_keys(g.cu_k, [cap, cap])
+    ob, lb = run_oracle(wl, geom=gb)
+    for s, L in enumerate(lens):
+        rows = slice(g.cu_q[s], g.cu_q[s + 1])
+        npad = (cap - L) * inc
+        el = np.exp(l[:, rows])
+        assert np.max(np.abs(lb[:, rows] - np.log(el + npad))) < 1e-12
+        factor = (el / (el + npad)).T[..., None]
+        assert np.max(np.abs(ob[rows] - o[rows] * factor)) < 1e-12
+
+
+def test_empty_segment_and_gap_rows(golden):
+    """Gap rows keep the sentinel bit for bit; a segment with no keys gets
+    O = 0 and LSE = -inf (PR #302)."""
+    wl = W.config1()
+    g = wl.geom
+    o, l = run_oracle(wl)
+    sent = golden["gap_rows_untouched"]["sentinel"]
+    empty = golden["empty_segment"]
+    for s in range(g.nseg):
+        q0, q1, uq = g.cu_q[s], g.cu_q[s + 1], g.used_q[s]
+        assert np.all(o[q0 + uq:q1] == sent) and np.all(l[:, q0 + uq:q1] == sent)
+        if g.used_k[s] == 0:
+            assert np.all(o[q0:q0 + uq] == empty["output"])
+            assert not np.signbit(o[q0:q0 + uq]).any()
+            assert np.all(l[:, q0:q0 + uq] == float(empty["lse"]))
+
+
+def test_gqa_equals_repeated_heads():
+    """Folded GQA (head h reads KV head h // G) equals MHA on K/V whose heads
+    are repeated G times in place (repeat_interleave)."""
+    wl = W.random_small(51, nseg=3, cap_q=10, cap_k=12, hq=6, hkv=2, d=8,
+                        causal=True, dtype=W.FP32)
+    g = wl.geom
+    o, l = run_oracle(wl)
+    kr, vr = np.repeat(wl.k, 3, axis=1), np.repeat(wl.v, 3, axis=1)
+    o2, l2 = oracle.attention_fwd(wl.q, kr, vr, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                                  float(g.scale), True, wl.out_init(), wl.lse_init(),
+                                  workers=1)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+def test_key_permutation_invariance():
+    """Without causal, the order of a segment's used keys does not matter."""
+    wl = W.random_small(52, nseg=2, cap_q=6, cap_k=15, hq=2, hkv=1, d=8,
+                        causal=False, dtype=W.FP32, lengths=([6, 4], [15, 11]))
+    g = wl.geom
+    o, l = run_oracle(wl)
+    perm = np.arange(g.total_k)
+    rng = np.random.default_rng(0)
+    for s in range(2):
+        a, b = g.cu_k[s], g.cu_k[s] + g.used_k[s]
+        perm[a:b] = rng.permutation(np.arange(a, b))
+    o2, l2 = oracle.attention_fwd(wl.q, wl.k[perm], wl.v[perm], g.cu_q, g.cu_k,
+                                  g.used_q, g.used_k, float(g.scale), False,
+                                  wl.out_init(), wl.lse_init(), workers=1)
+    assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(l - l2)) < 1e-12
+
+
+def test_segment_isolation_and_nan_gaps():
+    """NaN in gap rows of Q/K/V and different data in other segments leave a
+    segment's used rows bit-identical."""
+    wl = W.random_small(53, nseg=3, cap_q=9, cap_k=11, hq=4, hkv=2, d=8,
+                        causal=True, dtype=W.FP32, lengths=([5, 9, 3], [7, 4, 11]))
+    g = wl.geom
+    o, l = run_oracle(wl)
+    q, k, v = wl.q.copy(), wl.k.copy(), wl.v.copy()
+    for s in range(3):
+        q[g.cu_q[s] + g.used_q[s]:g.cu_q[s + 1]] = np.nan
+        k[g.cu_k[s] + g.used_k[s]:g.cu_k[s + 1]] = np.nan
+        v[g.cu_k[s] + g.used_k[s]:g.cu_k[s + 1]] = np.nan
+    q[g.cu_q[0]:g.cu_q[0] + 5] += 3.0       # perturb segment 0 only
+    k[g.cu_k[0]:g.cu_k[0] + 7] -= 1.0
+    o2, l2 = oracle.attention_fwd(q, k, v, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                                  float(g.scale), True, wl.out_init(), wl.lse_init(),
+                                  workers=1)
+    rows = slice(g.cu_q[1], g.cu_q[3])
+    assert np.array_equal(o[rows], o2[rows]) and np.array_equal(l[:, rows], l2[:, rows])
+    assert not np.isnan(o2).any() and not np.isnan(l2).any()
+
+
+# --- merge --------------------------------------------------------------------
+
+def _split_keys(g, cut_fracs):
+    """Key partitions of every segment: consecutive key ranges."""
+    parts = []
+    bounds = []
+    for s in range(g.nseg):
+        uk = int(g.used_k[s])
+        cuts = [0] + [int(round(f * uk)) for f in cut_fracs] + [uk]
+        bounds.append(cuts)
+    for p in range(len(cut_fracs) + 1):
+        starts = [int(g.cu_k[s]) + bounds[s][p] for s in range(g.nseg)]
+        used = [bounds[s][p + 1] - bounds[s][p] for s in range(g.nseg)]
+        cu = np.array(starts + [g.total_k], np.int32)
+        parts.append((cu, np.array(used, np.int32)))
+    return parts
+
+
+@pytest.mark.parametrize("cuts", [[0.5], [0.0, 0.3], [0.25, 0.5, 1.0]])
+def test_merge_of_partitions_equals_single_pass(cuts, golden):
+    """merge(partials of a key split) == one pass over all keys (PR #312)."""
+    assert golden["merge_of_partitions"]
+    wl = W.random_small(61, nseg=4, cap_q=7, cap_k=16, hq=4, hkv=2, d=8,
+                        causal=False, dtype=W.FP32, lengths=([7, 3, 0, 5], [16, 9, 5, 0]))
+    g = wl.geom
+    o, l = run_oracle(wl)
+    outs, lses = [], []
+    for cu, used in _split_keys(g, cuts):
+        op, lp = run_oracle(wl, geom=g.with_keys(cu, used))
+        outs.append(op)
+        lses.append(lp)
+    om, lm = oracle.lse_merge(outs, lses, g.cu_q, g.used_q, wl.out_init(), wl.lse_init())
+    assert np.array_equal(np.isinf(lm), np.isinf(l))
+    fin = np.isfinite(l)
+    assert np.max(np.abs(lm[fin] - l[fin])) < 1e-12
+    assert np.max(np.abs(om - o)) < 1e-12
+    # gap rows untouched by the merge
+    for s in range(g.nseg):
+        gap = slice(g.cu_q[s] + g.used_q[s], g.cu_q[s + 1])
+        assert np.all(om[gap] == W.SENTINEL) and np.all(lm[:, gap] == W.SENTINEL)
+
+
+def test_merge_closed_form_two_parts():
+    """Two partials with LSE a and b: weights e^a/(e^a+e^b), LSE ln(e^a+e^b)."""
+    a, b = 0.3, -1.2
+    o1 = np.array([[[1.0, -2.0]]])
+    o2 = np.array([[[4.0, 0.5]]])
+    l1, l2 = np.array([[a]]), np.array([[b]])
+    om, lm = oracle.lse_merge([o1, o2], [l1, l2], [0, 1], [1])
+    wa = math.exp(a) / (math.exp(a) + math.exp(b))
+    assert abs(lm[0, 0] - math.log(math.exp(a) + math.exp(b))) < 1e-15
+    assert np.allclose(om[0, 0], wa * o1[0, 0] + (1 - wa) * o2[0, 0], atol=1e-15, rtol=0)
+    # a partial that saw no key (LSE -inf) has weight 0; all -inf gives (0, -inf)
+    om, lm = oracle.lse_merge([o1, o2], [l1, np.array([[-np.inf]])], [0, 1], [1])
+    assert np.array_equal(om[0, 0], o1[0, 0]) and lm[0, 0] == a
+    om, lm = oracle.lse_merge([o1, o2], [np.array([[-np.inf]])] * 2, [0, 1], [1])
+    assert np.all(om == 0.0) and lm[0, 0] == -np.inf
+
+
+def test_flop_count_config1():
+    g = W.config1().geom
+    assert oracle.attention_flops(g.used_q, g.used_k, g.hq, g.d, g.dv, False) == 5_799_936
+    # causal counts only visible pairs: uq=3, uk=5 -> rows see 3, 4, 5 keys
+    assert oracle.attention_flops([3], [5], 1, 1, 1, True) == 12 * 4
+    assert oracle.attention_flops([5], [3], 1, 1, 1, True) == 6 * 4
