@@ -1,0 +1,222 @@
+"""Benchmark of the segmented varlen attention forward on one MI355X.
+
+Default workload: BF16 causal gapped replay, 64 segments of capacity 2048,
+used q/k lengths uniform in [0, 2048] (4 segments without keys), 32 q heads /
+8 KV heads, d = 128, bottom-right causal.  A step is one gvattn_fwd call
+(device plan + attention) over the resident inputs.  The metric is TFLOP/s
+over used rows: every visible (query, key) pair costs 4*d FLOPs per query
+head; masked, gap and padding work is never counted.
+
+Prints one JSON line.  ``--config N`` benches another workload (2, 4, 5:
+4 times the two partition launches plus the LSE merge).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CSRC = os.path.join(ROOT, "segmented_varlen_attention_amd", "csrc")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_causal_replay_64x2048_pmc.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the main kernel from the committed rocprofv3
+    --pmc summary, if it was taken on the current kernel sources."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic_json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("kernel_source_sha") == kernel_source_hash():
+                return rec
+    return None
+
+
+def algorithmic_bytes(geom, elem=2) -> int:
+    """Used Q + used O + LSE + used K + used V, each once."""
+    uq = int(np.sum(geom.used_q))
+    uk = int(np.sum(geom.used_k[geom.used_q > 0]))
+    return (uq * geom.hq * geom.d * elem * 2 + uq * geom.hq * 4
+            + uk * geom.hkv * geom.d * elem * 2)
+
+
+def cpu_baseline(wl, flops_fn, budget_segments: int):
+    """The oracle, as it stands, on a bounded sample of the workload."""
+    import oracle
+    g = wl.geom
+    order = [s for s in range(g.nseg) if g.used_q[s] > 0][:budget_segments]
+    workers = oracle.host_cores()
+    t0 = time.perf_counter()
+    oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k, float(g.scale),
+                         g.causal, workers=workers, segments=order)
+    dt = time.perf_counter() - t0
+    fl = flops_fn(g.used_q[order], g.used_k[order])
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"segments {order[0]}..{order[-1]} ({len(order)} of {g.nseg}), all "
+                      f"{g.hq} heads, {fl / 1e9:.1f} GFLOP in {dt:.1f} s, FP64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-segments", type=int, default=24)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import segmented_varlen_attention_amd as gv
+    from segmented_varlen_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    gv.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    wl = W.CONFIGS[args.config]()
+    g = wl.geom
+    log(f"[bench] workload {wl.name} generated in {time.time() - t0:.1f}s")
+
+    def flops_of(uq, uk):
+        pairs = 0
+        for a, b in zip(uq, uk):
+            a, b = int(a), int(b)
+            if a == 0 or b == 0:
+                continue
+            if g.causal:
+                i = np.arange(a)
+                pairs += int(np.clip(i + b - a + 1, 0, b).sum())
+            else:
+                pairs += a * b
+        return pairs * g.hq * (2 * g.d + 2 * g.dv)
+
+    flops = flops_of(g.used_q, g.used_k)
+    tdt = torch.bfloat16
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+    q, k, v = up(wl.q).to(tdt), up(wl.k).to(tdt), up(wl.v).to(tdt)
+    cu_q, used_q = up(g.cu_q), up(g.used_q)
+    out = torch.full((g.total_q, g.hq, g.dv), W.SENTINEL, dtype=tdt, device=dev)
+    lse = torch.full((g.hq, g.total_q), W.SENTINEL, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    if args.config == 4:
+        launches = [(up(cu), up(u)) for cu, u in wl.partitions]
+        parts = [(torch.empty_like(out), torch.empty_like(lse)) for _ in launches]
+        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, gv.GVATTN_BF16)
+               for _ in launches]
+    else:
+        launches = [(up(g.cu_k), up(g.used_k))]
+        parts = [(out, lse)]
+        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, gv.GVATTN_BF16)]
+
+    def step():
+        for (cu_k, used_k), (o, l), ws in zip(launches, parts, wss):
+            gv.gvattn_fwd(q, k, v, cu_q, cu_k, used_q, used_k, o, l, float(g.scale), g.causal,
+                          workspace=ws)
+        if args.config == 4:
+            gv.gvattn_lse_merge([p[0] for p in parts], [p[1] for p in parts], cu_q, used_q, out,
+                                lse)
+
+    def run_only():
+        (cu_k, used_k), (o, l), ws = launches[0], parts[0], wss[0]
+        gv.gvattn_fwd_run(q, k, v, cu_q, cu_k, used_q, used_k, o, l, float(g.scale), g.causal,
+                          ws)
+
+    if args.config == 4:
+        flops = sum(flops_of(g.used_q, u) for _, u in wl.partitions)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step")
+
+    # main attention kernel alone: the plan stays in the workspace
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    run_only()
+    k0.record(stream)
+    for _ in range(args.steps):
+        run_only()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = k0.elapsed_time(k1) / args.steps
+    kern_flops = flops_of(g.used_q, launches[0][1].cpu().numpy()) if args.config == 4 else flops
+    log(f"[bench] main kernel alone: {kern_ms:.4f} ms/launch")
+
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved = kern_flops / (kern_ms * 1e-3) / 1e12
+    traffic_rec = recorded_traffic() if args.config == 3 else None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": (traffic_rec["bytes_per_launch"] if traffic_rec else None)}
+    names = {2: "bf16_cfg_cross_attn_b2_4096q_text24_700_gqa32x8_d128",
+             3: "bf16_causal_gapped_replay_64x2048_gqa32x8_d128",
+             4: "bf16_multiview_8x8190q_32760k_2partitions_merge_gqa24x8_d128",
+             5: "bf16_gapped_16x16384_gqa16x4_d256"}
+    res = {
+        "metric": "gapped varlen attn fwd TFLOP/s (used rows) + % of MI355X bf16 MFMA peak",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": names[args.config], "segments": g.nseg,
+                   "used_q_rows": int(np.sum(g.used_q)), "hq": g.hq, "hkv": g.hkv, "d": g.d,
+                   "causal": bool(g.causal), "flop_per_step": flops,
+                   "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                   "algorithmic_hbm_bytes": algorithmic_bytes(g)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline and args.config == 3:
+        log("[bench] timing the oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_segments)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

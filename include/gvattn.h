@@ -1,0 +1,209 @@
+/*
+ * gvattn -- segmented ("gapped") variable-length attention forward and LSE
+ * merge for AMD Instinct MI355X (gfx950).  Plain C ABI: pointers and sizes
+ * only, no C++ or framework types.
+ *
+ * The operation (the sources are the pages this library implements):
+ *
+ *   cosmos-framework PR #302 ("gapped replay on GPUs FlashAttention-4 has no
+ *   kernels for"), section "What": Q, K and V are packed segment after
+ *   segment.  Segment s owns query rows [cu_q[s], cu_q[s+1]) and key rows
+ *   [cu_k[s], cu_k[s+1]) (its capacities) and uses only the prefixes of
+ *   length seqused_q[s] and seqused_k[s].  The used query rows of a segment
+ *   attend the used keys of the same segment only.  Rows past a segment's
+ *   used length are left as they are, and a segment with no keys gets a zero
+ *   output and a -inf log-sum-exp.
+ *
+ *   TensorRT-LLM issue #18687 ("Cosmos3 sequence-parallel path attends
+ *   zero-padded text K/V"), sections "actual behavior" and "additional
+ *   notes": keys past the used length are excluded by a key-padding mask,
+ *   never merely zeroed, because a zero key would add exp(0) = 1 to the
+ *   softmax denominator.
+ *
+ *   cosmos-framework PR #312 ("support SM120 replay with dense FA4
+ *   batches"), section "Problem and behavior": GQA folding, FP32 LSE, and
+ *   an FP32 LSE merge that combines the partial results of several
+ *   visibility partitions.
+ *
+ * Conventions (readings of what the pages leave open):
+ *   - query head h reads KV head h / (hq / hkv);
+ *   - causal masks are aligned bottom-right inside each segment: query row i
+ *     (0-based in the segment) sees key j iff j <= i + seqused_k - seqused_q;
+ *   - any row with no visible key (an empty segment, or a causal row above
+ *     the diagonal when seqused_k < seqused_q) gets O = +0 and LSE = -inf;
+ *   - LSE is the natural logarithm of sum_j exp(softmax_scale * q.k_j);
+ *   - layouts (row-major, innermost last):
+ *       Q   [total_q, hq,  d]      K [total_k, hkv, d]     V [total_k, hkv, d]
+ *       O   [total_q, hq,  d]      LSE float [hq, total_q]
+ *     Q, K, V and O share one element type (gvattn_dtype); LSE is fp32.
+ *
+ * Ownership and streams: every buffer is caller-owned device memory.  The
+ * library never allocates, frees, copies between host and device or
+ * synchronises (except gvattn_read_device_error, which is a debugging aid).
+ * All work is enqueued on `hip_stream` (a hipStream_t; NULL is the null
+ * stream) in argument order.  Calls on one workspace must not overlap.
+ *
+ * Errors: every host-checkable problem returns a status code before any
+ * work is enqueued.  Problems that depend on device data (a used length
+ * beyond its capacity, offsets out of range or decreasing, a segment that
+ * spans 2 GiB or more) cannot be seen without a synchronisation: the plan
+ * kernel skips such a segment (its rows are left untouched) and sets a bit
+ * in the workspace's device error word, which gvattn_read_device_error
+ * returns.
+ */
+#ifndef GVATTN_H
+#define GVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gvattn_status {
+  GVATTN_OK = 0,
+  GVATTN_ERR_INVALID_ARG = 1,  /* null pointer, negative size, hq % hkv != 0, bad scale ... */
+  GVATTN_ERR_UNSUPPORTED = 2,  /* head dim, dtype or partition count not built */
+  GVATTN_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small */
+  GVATTN_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} gvattn_status;
+
+typedef enum gvattn_dtype {
+  GVATTN_FP32 = 0,
+  GVATTN_BF16 = 1
+} gvattn_dtype;
+
+/* Device error word bits (see gvattn_read_device_error). */
+#define GVATTN_DEVERR_USED_Q 1   /* seqused_q[s] < 0 or > cu_q[s+1]-cu_q[s]  */
+#define GVATTN_DEVERR_USED_K 2   /* seqused_k[s] < 0 or > cu_k[s+1]-cu_k[s]  */
+#define GVATTN_DEVERR_OFFSETS 4  /* cu_* decreasing, negative or past total_* */
+#define GVATTN_DEVERR_RANGE 8    /* a segment's rows span 2 GiB or more      */
+#define GVATTN_DEVERR_PLAN 16    /* gvattn_fwd_run found no matching plan   */
+
+/* Largest partition count gvattn_lse_merge accepts. */
+#define GVATTN_MAX_PARTS 8
+
+/* Alignment the workspace pointer must have, in bytes. */
+#define GVATTN_WORKSPACE_ALIGN 256
+
+/*
+ * Bytes of device workspace gvattn_fwd needs for this geometry: a plan
+ * header, the tile work list and per-segment offsets.  It depends only on the
+ * host-known sizes, never on device data.  Returns 0 for invalid arguments.
+ */
+size_t gvattn_fwd_workspace_size(int32_t nseg, int32_t total_q, int32_t hq,
+                                 int32_t hkv, int32_t d, int32_t dtype);
+
+/*
+ * Segmented varlen attention forward: plan + run (PR #302, "What").
+ *
+ *   dtype            GVATTN_BF16 (MFMA path) or GVATTN_FP32.
+ *   q, k, v          device, layouts above; may hold anything (NaN
+ *                    included) in gap rows, which are never read into a
+ *                    result.
+ *   cu_seqlens_q/k   device int32 [nseg + 1], segment start offsets; the
+ *                    last entry bounds the last segment's capacity.
+ *                    Segments may leave rows between them.
+ *   seqused_q/k      device int32 [nseg], used prefix of each segment.
+ *   nseg             >= 0 (0 is a no-op).
+ *   total_q/total_k  rows of the Q/O and K/V buffers.
+ *   hq, hkv          heads, hq % hkv == 0.
+ *   d                head dim of Q, K and V: 64, 128 or 256.
+ *   softmax_scale    finite and > 0 (typically 1/sqrt(d)).
+ *   causal           0 or 1 (bottom-right within each segment).
+ *   out, lse         device, written for used rows only; every other row is
+ *                    left bit-for-bit as it was.  Must not overlap q/k/v.
+ *   workspace        device, GVATTN_WORKSPACE_ALIGN-aligned, at least
+ *                    gvattn_fwd_workspace_size(...) bytes.
+ *   hip_stream       hipStream_t to enqueue on.
+ */
+int gvattn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+               const int32_t* seqused_q, const int32_t* seqused_k,
+               int32_t nseg, int32_t total_q, int32_t total_k,
+               int32_t hq, int32_t hkv, int32_t d,
+               float softmax_scale, int32_t causal,
+               void* out, float* lse,
+               void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * The two halves of gvattn_fwd, for callers that replay one geometry many
+ * times (PR #302, "What": the gather is built once per launch and fold, so
+ * segment lengths are read once per plan rather than at every step).
+ *
+ * gvattn_fwd_plan reads only the geometry arrays and writes the sorted tile
+ * work list into the workspace.  gvattn_fwd_run takes the same arguments as
+ * gvattn_fwd and runs the attention on the plan found in the workspace; the
+ * geometry arrays must hold the values the plan was built from.  A plan
+ * built for a different tile shape, head count, causal flag or segment count
+ * is detected on the device: the run writes nothing and sets
+ * GVATTN_DEVERR_PLAN.
+ */
+int gvattn_fwd_plan(int32_t dtype,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    const int32_t* seqused_q, const int32_t* seqused_k,
+                    int32_t nseg, int32_t total_q, int32_t total_k,
+                    int32_t hq, int32_t hkv, int32_t d, int32_t causal,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                   const int32_t* seqused_q, const int32_t* seqused_k,
+                   int32_t nseg, int32_t total_q, int32_t total_k,
+                   int32_t hq, int32_t hkv, int32_t d,
+                   float softmax_scale, int32_t causal,
+                   void* out, float* lse,
+                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * FP32 LSE merge of nparts partial results over key partitions (PR #312,
+ * "Problem and behavior").  For every used row (rows [cu_seqlens_q[s],
+ * cu_seqlens_q[s] + seqused_q[s])) and head, in FP32:
+ *   m = max_p LSE_p;  m = -inf  ->  O = 0, LSE = -inf;
+ *   otherwise w_p = exp(LSE_p - m), W = sum_p w_p,
+ *             LSE = m + ln W,  O = sum_p (w_p / W) O_p.
+ * A NaN in any LSE_p makes that row's O and LSE NaN.  Gap rows are left
+ * untouched.
+ *
+ *   nparts         1 .. GVATTN_MAX_PARTS.
+ *   part_out       HOST array of nparts device pointers, each
+ *                  [total_q, hq, d] of part_dtype.
+ *   part_lse       HOST array of nparts device pointers, each fp32
+ *                  [hq, total_q].
+ *   part_dtype     element type of the partial outputs.
+ *   out_dtype      element type of `out`.
+ *   cu_seqlens_q   device int32 [nseg + 1]; seqused_q device int32 [nseg].
+ *   out, lse       device; may alias part_out[0] / part_lse[0] (each row and
+ *                  head is read completely before it is written), no other
+ *                  overlap.
+ *   device_error   optional device int32; invalid segments are skipped and
+ *                  GVATTN_DEVERR_* bits are OR-ed into it.  May be NULL.
+ */
+int gvattn_lse_merge(int32_t nparts, const void* const* part_out,
+                     const float* const* part_lse, int32_t part_dtype,
+                     int32_t out_dtype,
+                     const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                     int32_t nseg, int32_t total_q, int32_t hq, int32_t d,
+                     void* out, float* lse, int32_t* device_error,
+                     void* hip_stream);
+
+/* Static text for a gvattn_status value. */
+const char* gvattn_status_string(int status);
+
+/*
+ * Debugging aid: waits for `hip_stream`, then copies the device error word
+ * of `workspace` (GVATTN_DEVERR_* bits of the last plan and the runs on it)
+ * into *err_out.  Synchronises; not for the hot path.
+ */
+int gvattn_read_device_error(const void* workspace, void* hip_stream,
+                             int32_t* err_out);
+
+/* Library ABI version (major * 100 + minor). */
+int gvattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GVATTN_H */

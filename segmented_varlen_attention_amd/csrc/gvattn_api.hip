@@ -1,0 +1,267 @@
+// C ABI of gvattn: argument validation, workspace layout, kernel dispatch.
+// Every host-checkable problem is rejected before any HIP call, so the
+// validation paths run (and are tested) on machines without a GPU.
+#include <math.h>
+
+#include <mutex>
+#include <unordered_map>
+
+#include "gvattn_internal.h"
+
+namespace gvattn {
+
+int persistent_grid(const void* kernel, int threads, int64_t max_work) {
+  if (max_work <= 0) return 0;
+  struct Key {
+    const void* k;
+    int dev;
+    bool operator==(const Key& o) const { return k == o.k && dev == o.dev; }
+  };
+  struct Hash {
+    size_t operator()(const Key& k) const {
+      return std::hash<const void*>()(k.k) ^ (std::hash<int>()(k.dev) << 1);
+    }
+  };
+  static std::mutex mu;
+  static std::unordered_map<Key, int, Hash> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int slots = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(Key{kernel, dev});
+    if (it != cache.end()) {
+      slots = it->second;
+    } else {
+      int per_cu = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+        return -1;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+      slots = (per_cu > 0 ? per_cu : 1) * cus;
+      cache.emplace(Key{kernel, dev}, slots);
+    }
+  }
+  return (int)(max_work < slots ? max_work : slots);
+}
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool dtype_ok(int32_t dtype) { return dtype == GVATTN_FP32 || dtype == GVATTN_BF16; }
+bool dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+int esize(int32_t dtype) { return dtype == GVATTN_FP32 ? 4 : 2; }
+
+int check_sizes(int32_t dtype, int32_t nseg, int32_t total_q, int32_t total_k, int32_t hq,
+                int32_t hkv, int32_t d, int32_t causal) {
+  if (!dtype_ok(dtype)) return GVATTN_ERR_UNSUPPORTED;
+  if (nseg < 0 || total_q < 0 || total_k < 0 || hq <= 0 || hkv <= 0) return GVATTN_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return GVATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return GVATTN_ERR_INVALID_ARG;
+  if (!dim_ok(d)) return GVATTN_ERR_UNSUPPORTED;
+  // one packed row (all heads) must stay well inside a 32-bit byte offset
+  if ((int64_t)hq * d * esize(dtype) > (int64_t(1) << 24)) return GVATTN_ERR_UNSUPPORTED;
+  return GVATTN_OK;
+}
+
+int check_workspace(const void* ws, size_t bytes, int32_t nseg, int32_t total_q, int rows) {
+  if (ws == nullptr) return GVATTN_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % GVATTN_WORKSPACE_ALIGN != 0) return GVATTN_ERR_WORKSPACE;
+  if (bytes < workspace_bytes(nseg, total_q, rows)) return GVATTN_ERR_WORKSPACE;
+  return GVATTN_OK;
+}
+
+Geometry make_geom(const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
+                   const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
+                   int32_t hq, int32_t hkv, int32_t d, int32_t causal) {
+  Geometry g;
+  g.cu_q = cu_q;
+  g.cu_k = cu_k;
+  g.used_q = used_q;
+  g.used_k = used_k;
+  g.nseg = nseg;
+  g.total_q = total_q;
+  g.total_k = total_k;
+  g.hq = hq;
+  g.hkv = hkv;
+  g.d = d;
+  g.causal = causal;
+  return g;
+}
+
+int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
+  const TileShape t = choose_shape(dtype, g.hq, g.hkv, g.d);
+  PlanArgs a;
+  a.g = g;
+  a.ws = view_workspace(ws, g.nseg, g.total_q, t.rows);
+  a.rows = t.rows;
+  a.max_tiles = (int32_t)max_tiles(g.nseg, g.total_q, t.rows);
+  a.key = plan_key(t.rows, g.causal, g.nseg);
+  a.q_row_bytes = (int64_t)g.hq * g.d * esize(dtype);
+  a.k_row_bytes = (int64_t)g.hkv * g.d * esize(dtype);
+  return launch_plan(a, stream) == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
+}
+
+int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const void* v,
+           float scale, void* out, float* lse, void* ws, hipStream_t stream) {
+  const TileShape t = choose_shape(dtype, g.hq, g.hkv, g.d);
+  FwdArgs a;
+  a.g = g;
+  a.ws = view_workspace(ws, g.nseg, g.total_q, t.rows);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.scale_log2 = scale * kLog2e;
+  a.key = plan_key(t.rows, g.causal, g.nseg);
+  a.n_head_chunks = g.hq / t.gf;
+  const int64_t max_work = max_tiles(g.nseg, g.total_q, t.rows) * a.n_head_chunks;
+  bool ok = false;
+  hipError_t e = (dtype == GVATTN_BF16) ? launch_fwd_bf16(a, t, max_work, stream, &ok)
+                                        : launch_fwd_fp32(a, t, max_work, stream, &ok);
+  if (!ok) return GVATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
+}
+
+int check_fwd_args(int32_t dtype, const void* q, const void* k, const void* v,
+                   const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
+                   const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
+                   int32_t hq, int32_t hkv, int32_t d, float scale, int32_t causal,
+                   void* out, float* lse, void* ws, size_t ws_bytes) {
+  int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, causal);
+  if (rc != GVATTN_OK) return rc;
+  if (!(scale > 0.f) || !isfinite(scale)) return GVATTN_ERR_INVALID_ARG;
+  if (nseg == 0) return GVATTN_OK;
+  if (!q || !k || !v || !cu_q || !cu_k || !used_q || !used_k || !out || !lse)
+    return GVATTN_ERR_INVALID_ARG;
+  const TileShape t = choose_shape(dtype, hq, hkv, d);
+  return check_workspace(ws, ws_bytes, nseg, total_q, t.rows);
+}
+
+}  // namespace
+}  // namespace gvattn
+
+using namespace gvattn;
+
+extern "C" {
+
+size_t gvattn_fwd_workspace_size(int32_t nseg, int32_t total_q, int32_t hq, int32_t hkv,
+                                 int32_t d, int32_t dtype) {
+  if (check_sizes(dtype, nseg, total_q, 0, hq, hkv, d, 0) != GVATTN_OK) return 0;
+  const TileShape t = choose_shape(dtype, hq, hkv, d);
+  return workspace_bytes(nseg, total_q, t.rows);
+}
+
+int gvattn_fwd_plan(int32_t dtype, const int32_t* cu_q, const int32_t* cu_k,
+                    const int32_t* used_q, const int32_t* used_k, int32_t nseg,
+                    int32_t total_q, int32_t total_k, int32_t hq, int32_t hkv, int32_t d,
+                    int32_t causal, void* workspace, size_t workspace_bytes_,
+                    void* hip_stream) {
+  int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, causal);
+  if (rc != GVATTN_OK) return rc;
+  if (nseg == 0) return GVATTN_OK;
+  if (!cu_q || !cu_k || !used_q || !used_k) return GVATTN_ERR_INVALID_ARG;
+  const TileShape t = choose_shape(dtype, hq, hkv, d);
+  rc = check_workspace(workspace, workspace_bytes_, nseg, total_q, t.rows);
+  if (rc != GVATTN_OK) return rc;
+  const Geometry g = make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, causal);
+  return do_plan(dtype, g, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
+                   const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
+                   const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
+                   int32_t hq, int32_t hkv, int32_t d, float softmax_scale, int32_t causal,
+                   void* out, float* lse, void* workspace, size_t workspace_bytes_,
+                   void* hip_stream) {
+  int rc = check_fwd_args(dtype, q, k, v, cu_q, cu_k, used_q, used_k, nseg, total_q, total_k,
+                          hq, hkv, d, softmax_scale, causal, out, lse, workspace,
+                          workspace_bytes_);
+  if (rc != GVATTN_OK || nseg == 0) return rc;
+  const Geometry g = make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, causal);
+  return do_run(dtype, g, q, k, v, softmax_scale, out, lse, workspace,
+                static_cast<hipStream_t>(hip_stream));
+}
+
+int gvattn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+               const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
+               const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
+               int32_t hq, int32_t hkv, int32_t d, float softmax_scale, int32_t causal,
+               void* out, float* lse, void* workspace, size_t workspace_bytes_,
+               void* hip_stream) {
+  int rc = check_fwd_args(dtype, q, k, v, cu_q, cu_k, used_q, used_k, nseg, total_q, total_k,
+                          hq, hkv, d, softmax_scale, causal, out, lse, workspace,
+                          workspace_bytes_);
+  if (rc != GVATTN_OK || nseg == 0) return rc;
+  const Geometry g = make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, causal);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  rc = do_plan(dtype, g, workspace, s);
+  if (rc != GVATTN_OK) return rc;
+  return do_run(dtype, g, q, k, v, softmax_scale, out, lse, workspace, s);
+}
+
+int gvattn_lse_merge(int32_t nparts, const void* const* part_out, const float* const* part_lse,
+                     int32_t part_dtype, int32_t out_dtype, const int32_t* cu_q,
+                     const int32_t* used_q, int32_t nseg, int32_t total_q, int32_t hq,
+                     int32_t d, void* out, float* lse, int32_t* device_error,
+                     void* hip_stream) {
+  if (!dtype_ok(part_dtype) || !dtype_ok(out_dtype)) return GVATTN_ERR_UNSUPPORTED;
+  if (nparts < 1) return GVATTN_ERR_INVALID_ARG;
+  if (nparts > GVATTN_MAX_PARTS) return GVATTN_ERR_UNSUPPORTED;
+  if (nseg < 0 || total_q < 0 || hq <= 0) return GVATTN_ERR_INVALID_ARG;
+  if (!dim_ok(d)) return GVATTN_ERR_UNSUPPORTED;
+  if (nseg == 0 || total_q == 0) return GVATTN_OK;
+  if (!part_out || !part_lse || !cu_q || !used_q || !out || !lse) return GVATTN_ERR_INVALID_ARG;
+  MergeArgs a;
+  for (int p = 0; p < GVATTN_MAX_PARTS; ++p) {
+    a.part_out[p] = nullptr;
+    a.part_lse[p] = nullptr;
+  }
+  for (int p = 0; p < nparts; ++p) {
+    if (!part_out[p] || !part_lse[p]) return GVATTN_ERR_INVALID_ARG;
+    a.part_out[p] = part_out[p];
+    a.part_lse[p] = part_lse[p];
+  }
+  a.nparts = nparts;
+  a.cu_q = cu_q;
+  a.used_q = used_q;
+  a.nseg = nseg;
+  a.total_q = total_q;
+  a.hq = hq;
+  a.d = d;
+  a.out = out;
+  a.lse = lse;
+  a.err = device_error;
+  bool ok = false;
+  hipError_t e = launch_merge(a, part_dtype, out_dtype, static_cast<hipStream_t>(hip_stream), &ok);
+  if (!ok) return GVATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
+}
+
+const char* gvattn_status_string(int status) {
+  switch (status) {
+    case GVATTN_OK: return "GVATTN_OK";
+    case GVATTN_ERR_INVALID_ARG: return "GVATTN_ERR_INVALID_ARG: invalid argument";
+    case GVATTN_ERR_UNSUPPORTED: return "GVATTN_ERR_UNSUPPORTED: head dim, dtype or partition count not supported";
+    case GVATTN_ERR_WORKSPACE: return "GVATTN_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case GVATTN_ERR_HIP: return "GVATTN_ERR_HIP: HIP runtime error";
+    default: return "unknown gvattn status";
+  }
+}
+
+int gvattn_read_device_error(const void* workspace, void* hip_stream, int32_t* err_out) {
+  if (!workspace || !err_out) return GVATTN_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const PlanHeader* h = static_cast<const PlanHeader*>(workspace);
+  int32_t v = 0;
+  if (hipStreamSynchronize(s) != hipSuccess) return GVATTN_ERR_HIP;
+  if (hipMemcpy(&v, &h->err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return GVATTN_ERR_HIP;
+  *err_out = v;
+  return GVATTN_OK;
+}
+
+int gvattn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+// Internal definitions shared by the gvattn HIP sources: workspace layout,
+// tile shapes, kernel argument blocks and small device helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gvattn.h"
+
+namespace gvattn {
+
+// ---------------------------------------------------------------------------
+// Workspace: [PlanHeader (256 B)] [tile list: int2 x max_tiles]
+//            [per-segment tile offsets: int32 x (nseg + 1)]
+// A tile is (segment, first row in the segment); the list is sorted by
+// decreasing number of key tiles so that the persistent kernel takes the
+// longest work first.
+// ---------------------------------------------------------------------------
+struct PlanHeader {
+  int32_t n_tiles;
+  int32_t err;
+  uint32_t key;
+  int32_t rows_per_tile;
+  int32_t reserved[60];
+};
+static_assert(sizeof(PlanHeader) == 256, "plan header is 256 bytes");
+
+constexpr int kKeyTile = 64;          // keys per LDS tile (BN)
+constexpr int kCostBuckets = 2048;    // sort buckets (key tiles per q-tile)
+
+// Tile shape of one forward variant.
+struct TileShape {
+  int rows;   // query rows per tile (per head)
+  int gf;     // query heads folded into one workgroup (divides hq / hkv)
+  int waves;  // waves per workgroup
+};
+
+// Folding: the workgroup owns `gf` consecutive query heads of one KV group
+// and 32 * rb query rows of each, one wave per (head, 32-row block).
+inline TileShape choose_shape(int dtype, int hq, int hkv, int d) {
+  (void)d;
+  TileShape t{};
+  if (dtype == GVATTN_FP32) {
+    t.rows = 16;
+    t.gf = 1;
+    t.waves = 4;
+    return t;
+  }
+  const int g = hq / hkv;
+  int gf = 1;
+  if (g % 4 == 0) gf = 4;
+  else if (g % 3 == 0) gf = 3;
+  else if (g % 2 == 0) gf = 2;
+  const int rb = (gf == 3) ? 1 : 4 / gf;
+  t.rows = 32 * rb;
+  t.gf = gf;
+  t.waves = gf * rb;
+  return t;
+}
+
+inline uint32_t plan_key(int rows, int causal, int nseg) {
+  uint32_t h = 2166136261u;
+  auto mix = [&h](uint32_t x) { h = (h ^ x) * 16777619u; };
+  mix((uint32_t)rows);
+  mix((uint32_t)causal);
+  mix((uint32_t)nseg);
+  return h | 1u;  // never 0, so a zeroed workspace never matches
+}
+
+inline int64_t max_tiles(int64_t nseg, int64_t total_q, int rows) {
+  return total_q / rows + nseg + 1;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline size_t workspace_bytes(int64_t nseg, int64_t total_q, int rows) {
+  size_t b = sizeof(PlanHeader);
+  b += align_up((size_t)max_tiles(nseg, total_q, rows) * 8, 256);
+  b += align_up((size_t)(nseg + 1) * 4, 256);
+  return b;
+}
+
+struct WorkspaceView {
+  PlanHeader* header;
+  int2* tiles;
+  int32_t* seg_tile_off;
+};
+
+inline WorkspaceView view_workspace(void* ws, int64_t nseg, int64_t total_q, int rows) {
+  WorkspaceView v;
+  char* p = static_cast<char*>(ws);
+  v.header = reinterpret_cast<PlanHeader*>(p);
+  p += sizeof(PlanHeader);
+  v.tiles = reinterpret_cast<int2*>(p);
+  p += align_up((size_t)max_tiles(nseg, total_q, rows) * 8, 256);
+  v.seg_tile_off = reinterpret_cast<int32_t*>(p);
+  return v;
+}
+
+// Geometry shared by plan and forward kernels.
+struct Geometry {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* used_q;
+  const int32_t* used_k;
+  int32_t nseg;
+  int32_t total_q;
+  int32_t total_k;
+  int32_t hq;
+  int32_t hkv;
+  int32_t d;
+  int32_t causal;
+};
+
+struct PlanArgs {
+  Geometry g;
+  WorkspaceView ws;
+  int32_t rows;        // rows per tile
+  int32_t max_tiles;   // capacity of the tile list
+  uint32_t key;
+  int64_t q_row_bytes;  // bytes of one packed Q/O row (all heads)
+  int64_t k_row_bytes;  // bytes of one packed K/V row (all heads)
+};
+
+struct FwdArgs {
+  Geometry g;
+  WorkspaceView ws;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  float scale_log2;     // softmax_scale * log2(e)
+  uint32_t key;
+  int32_t n_head_chunks;  // hq / gf
+};
+
+struct MergeArgs {
+  const void* part_out[GVATTN_MAX_PARTS];
+  const float* part_lse[GVATTN_MAX_PARTS];
+  int32_t nparts;
+  const int32_t* cu_q;
+  const int32_t* used_q;
+  int32_t nseg;
+  int32_t total_q;
+  int32_t hq;
+  int32_t d;
+  void* out;
+  float* lse;
+  int32_t* err;
+};
+
+// Host-side launchers (one translation unit each).
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, const TileShape& t, int64_t max_work,
+                           hipStream_t s, bool* supported);
+hipError_t launch_fwd_fp32(const FwdArgs& a, const TileShape& t, int64_t max_work,
+                           hipStream_t s, bool* supported);
+hipError_t launch_merge(const MergeArgs& a, int part_dtype, int out_dtype, hipStream_t s,
+                        bool* supported);
+
+// Persistent grid size for a kernel: resident blocks per CU x CUs, capped by
+// the work available.
+int persistent_grid(const void* kernel, int threads, int64_t max_work);
+
+}  // namespace gvattn
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+#if defined(__HIPCC__)
+namespace gvattn {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource: loads at byte offsets >= num_bytes return zero and
+// stores there are dropped, which is how ragged tiles, gap rows and the
+// ends of buffers are guarded.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)num_bytes, 0x00020000);
+}
+
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+__device__ inline float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+__device__ inline void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane (lane ^ 32).
+__device__ inline float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+}  // namespace dev
+}  // namespace gvattn
+#endif

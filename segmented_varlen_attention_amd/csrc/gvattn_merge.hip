@@ -1,0 +1,192 @@
+// FP32 LSE merge of partial attention results over key partitions
+// (cosmos-framework PR #312, "Problem and behavior": visibility partitions
+// are computed separately and combined by an FP32 LSE merge).
+//
+// For each used row and head, in FP32:
+//   m = max_p LSE_p;  m = -inf -> O = 0, LSE = -inf;
+//   else w_p = exp(LSE_p - m), W = sum_p w_p, LSE = m + ln W,
+//        O = sum_p (w_p / W) O_p.
+// The kernel is HBM-bound: D/8 lanes own one (row, head) and move it with
+// 16-byte vector loads/stores; consecutive (row, head) pairs are consecutive
+// rows of one head, so the LSE traffic is contiguous too.  Gap rows are
+// skipped (left untouched).  Each (row, head) is fully read before it is
+// written by the same lanes, so `out` may alias part_out[0].
+#include <math.h>
+
+#include "gvattn_internal.h"
+
+namespace gvattn {
+namespace {
+
+using namespace dev;
+
+constexpr int kThreads = 256;
+
+template <typename T> struct Vec8;
+template <> struct Vec8<__bf16> {
+  static __device__ __forceinline__ void load(const void* p, float* f) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __builtin_bit_cast(float, v[i] << 16);
+      f[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(void* p, const float* f) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (__bf16)f[i];
+    *reinterpret_cast<bf16x8*>(p) = o;
+  }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const void* p, float* f) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+    const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = a[i];
+      f[4 + i] = b[i];
+    }
+  }
+  static __device__ __forceinline__ void store(void* p, const float* f) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = f[i];
+      b[i] = f[4 + i];
+    }
+    reinterpret_cast<f32x4*>(p)[0] = a;
+    reinterpret_cast<f32x4*>(p)[1] = b;
+  }
+};
+
+// Largest s in [0, nseg) with cu[s] <= row (cu assumed non-decreasing;
+// callers re-check membership).
+__device__ __forceinline__ int find_segment(const int32_t* cu, int nseg, int row) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= row) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename TIn, typename TOut, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  constexpr int LPP = D / 8;              // lanes per (row, head)
+  constexpr int PPB = kThreads / LPP;     // pairs per block per step
+  const int sub = threadIdx.x % LPP;
+  const int slot = threadIdx.x / LPP;
+  const int64_t npairs = (int64_t)a.hq * a.total_q;
+
+  // segment validation (block 0): report, the per-row checks below skip
+  if (blockIdx.x == 0 && a.err != nullptr) {
+    for (int s = threadIdx.x; s < a.nseg; s += kThreads) {
+      const int c0 = a.cu_q[s], c1 = a.cu_q[s + 1], u = a.used_q[s];
+      int e = 0;
+      if (c0 < 0 || c1 < c0 || c1 > a.total_q) e |= GVATTN_DEVERR_OFFSETS;
+      else if (u < 0 || u > c1 - c0) e |= GVATTN_DEVERR_USED_Q;
+      if (e) atomicOr(a.err, e);
+    }
+  }
+
+  for (int64_t base = (int64_t)blockIdx.x * PPB; base < npairs; base += (int64_t)gridDim.x * PPB) {
+    const int64_t pi = base + slot;
+    if (pi >= npairs) continue;
+    const int head = (int)(pi / a.total_q);
+    const int row = (int)(pi - (int64_t)head * a.total_q);
+    const int s = find_segment(a.cu_q, a.nseg, row);
+    const int c0 = a.cu_q[s], c1 = a.cu_q[s + 1], u = a.used_q[s];
+    if (c0 < 0 || c1 < c0 || c1 > a.total_q || u < 0 || u > c1 - c0) continue;
+    if (row < c0 || row >= c0 + u) continue;
+
+    const int64_t lidx = (int64_t)head * a.total_q + row;
+    float L[GVATTN_MAX_PARTS];
+    float m = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int p = 0; p < GVATTN_MAX_PARTS; ++p) {
+      if (p < a.nparts) {
+        L[p] = a.part_lse[p][lidx];
+        nan |= (L[p] != L[p]);
+        m = fmaxf(m, L[p]);
+      }
+    }
+    const int64_t eoff = ((int64_t)row * a.hq + head) * D + sub * 8;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    float lse_out;
+    if (nan) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = NAN;
+      lse_out = NAN;
+    } else if (m == -INFINITY) {
+      lse_out = -INFINITY;
+    } else {
+      constexpr float kLog2e = 1.4426950408889634f;
+      float wsum = 0.f;
+      float wp[GVATTN_MAX_PARTS];
+#pragma unroll
+      for (int p = 0; p < GVATTN_MAX_PARTS; ++p) {
+        wp[p] = 0.f;
+        if (p < a.nparts) {
+          wp[p] = __builtin_amdgcn_exp2f((L[p] - m) * kLog2e);
+          wsum += wp[p];
+        }
+      }
+      const float inv = 1.f / wsum;
+#pragma unroll
+      for (int p = 0; p < GVATTN_MAX_PARTS; ++p) {
+        if (p < a.nparts) {
+          float f[8];
+          Vec8<TIn>::load(static_cast<const TIn*>(a.part_out[p]) + eoff, f);
+          const float wn = wp[p] * inv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wn, f[i], acc[i]);
+        }
+      }
+      lse_out = m + logf(wsum);
+    }
+    Vec8<TOut>::store(static_cast<TOut*>(a.out) + eoff, acc);
+    if (sub == 0) a.lse[lidx] = lse_out;
+  }
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_t(const MergeArgs& a, hipStream_t s, bool* ok) {
+  const void* k = nullptr;
+  switch (a.d) {
+    case 64: k = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, 64>); break;
+    case 128: k = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, 128>); break;
+    case 256: k = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, 256>); break;
+    default: *ok = false; return hipSuccess;
+  }
+  *ok = true;
+  const int ppb = kThreads / (a.d / 8);
+  const int64_t need = ((int64_t)a.hq * a.total_q + ppb - 1) / ppb;
+  const int grid = persistent_grid(k, kThreads, need > 0 ? need : 1);
+  if (grid <= 0) return hipSuccess;
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((merge_kernel<TIn, TOut, 64>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((merge_kernel<TIn, TOut, 128>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((merge_kernel<TIn, TOut, 256>), dim3(grid), dim3(kThreads), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, int part_dtype, int out_dtype, hipStream_t s,
+                        bool* supported) {
+  if (part_dtype == GVATTN_BF16 && out_dtype == GVATTN_BF16) return launch_t<__bf16, __bf16>(a, s, supported);
+  if (part_dtype == GVATTN_BF16 && out_dtype == GVATTN_FP32) return launch_t<__bf16, float>(a, s, supported);
+  if (part_dtype == GVATTN_FP32 && out_dtype == GVATTN_BF16) return launch_t<float, __bf16>(a, s, supported);
+  if (part_dtype == GVATTN_FP32 && out_dtype == GVATTN_FP32) return launch_t<float, float>(a, s, supported);
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace gvattn

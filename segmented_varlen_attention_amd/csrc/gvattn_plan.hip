@@ -1,0 +1,161 @@
+// Plan kernel: builds the work list of the forward on the device, so the
+// host never reads segment lengths (the PR #302 review objects to host
+// syncs that read them back).
+//
+// One workgroup of 1024 threads:
+//   1. validates every segment and counts its query tiles, ceil(used_q/R);
+//      an invalid segment gets no tiles and sets a device error bit;
+//   2. prefix-sums the counts into per-segment tile offsets;
+//   3. histograms the tiles by cost = number of 64-key tiles their rows see
+//      (under bottom-right causal the last row of the tile sees the most);
+//   4. scatters (segment, first row) pairs into cost-descending order, so
+//      the persistent forward kernel starts the longest tiles first.
+// The order inside one cost bucket depends on atomics, but each tile's
+// result does not depend on the order, so outputs are deterministic.
+#include "gvattn_internal.h"
+
+namespace gvattn {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+template <typename T>
+__device__ T block_exclusive_scan(T x, T* tmp, T* total) {
+  const int t = threadIdx.x;
+  tmp[t] = x;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const T y = (t >= off) ? tmp[t - off] : T(0);
+    __syncthreads();
+    tmp[t] += y;
+    __syncthreads();
+  }
+  const T incl = tmp[t];
+  *total = tmp[kPlanThreads - 1];
+  __syncthreads();
+  return incl - x;
+}
+
+__device__ int segment_error(const PlanArgs& a, int s) {
+  const Geometry& g = a.g;
+  const int cq0 = g.cu_q[s], cq1 = g.cu_q[s + 1];
+  const int ck0 = g.cu_k[s], ck1 = g.cu_k[s + 1];
+  const int uq = g.used_q[s], uk = g.used_k[s];
+  if (cq0 < 0 || cq1 < cq0 || cq1 > g.total_q || ck0 < 0 || ck1 < ck0 || ck1 > g.total_k)
+    return GVATTN_DEVERR_OFFSETS;
+  int err = 0;
+  if (uq < 0 || uq > cq1 - cq0) err |= GVATTN_DEVERR_USED_Q;
+  if (uk < 0 || uk > ck1 - ck0) err |= GVATTN_DEVERR_USED_K;
+  // Tiles may run up to 256 rows past a segment's capacity before the
+  // bounds-checked loads reject them; keep every such offset below 2^31.
+  if ((int64_t)(cq1 - cq0 + 256) * a.q_row_bytes >= (int64_t(1) << 31) ||
+      (int64_t)(ck1 - ck0 + 256) * a.k_row_bytes >= (int64_t(1) << 31))
+    err |= GVATTN_DEVERR_RANGE;
+  return err;
+}
+
+// Largest s with seg_off[s] <= t (t < seg_off[nseg]).
+__device__ int find_segment(const int32_t* seg_off, int nseg, int t) {
+  int lo = 0, hi = nseg;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg_off[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ int tile_bucket(const PlanArgs& a, int s, int row0) {
+  const int uq = a.g.used_q[s], uk = a.g.used_k[s];
+  int kend = uk;
+  if (a.g.causal) {
+    const int r_last = min(row0 + a.rows, uq) - 1;
+    kend = max(0, min(uk, r_last + uk - uq + 1));
+  }
+  const int ntk = (kend + kKeyTile - 1) / kKeyTile;
+  return min(ntk, kCostBuckets - 1);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ long long tmp64[kPlanThreads];
+  __shared__ int tmp[kPlanThreads];
+  __shared__ int hist[kCostBuckets];
+  __shared__ int s_err;
+  const int tid = threadIdx.x;
+  const int nseg = a.g.nseg;
+  int32_t* seg_off = a.ws.seg_tile_off;
+
+  for (int b = tid; b < kCostBuckets; b += kPlanThreads) hist[b] = 0;
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+
+  // 1-2. tile counts and their offsets.  Segments whose capacities
+  // overlap can claim more tiles than the list holds; the whole plan is
+  // then rejected (no tiles) rather than written past the workspace.
+  long long carry = 0;
+  for (int base = 0; base < nseg; base += kPlanThreads) {
+    const int s = base + tid;
+    long long cnt = 0;
+    if (s < nseg) {
+      const int err = segment_error(a, s);
+      if (err) atomicOr(&s_err, err);
+      else cnt = (a.g.used_q[s] + a.rows - 1) / a.rows;
+    }
+    long long tot;
+    const long long excl = block_exclusive_scan<long long>(cnt, tmp64, &tot);
+    if (s < nseg) seg_off[s] = (int32_t)min(carry + excl, (long long)a.max_tiles);
+    carry += tot;
+  }
+  int n_tiles = (int)min(carry, (long long)a.max_tiles);
+  if (carry > a.max_tiles) {
+    n_tiles = 0;
+    if (tid == 0) s_err |= GVATTN_DEVERR_OFFSETS;
+  }
+  if (tid == 0) seg_off[nseg] = n_tiles;
+  __threadfence_block();
+  __syncthreads();
+
+  // 3. cost histogram
+  for (int t = tid; t < n_tiles; t += kPlanThreads) {
+    const int s = find_segment(seg_off, nseg, t);
+    const int row0 = (t - seg_off[s]) * a.rows;
+    atomicAdd(&hist[tile_bucket(a, s, row0)], 1);
+  }
+  __syncthreads();
+
+  // bucket start positions, most expensive bucket first
+  static_assert(kCostBuckets == 2 * kPlanThreads, "two buckets per thread");
+  const int b_hi = kCostBuckets - 1 - 2 * tid;  // visited first
+  const int b_lo = b_hi - 1;
+  const int c_hi = hist[b_hi], c_lo = hist[b_lo];
+  int tot;
+  const int excl = block_exclusive_scan<int>(c_hi + c_lo, tmp, &tot);
+  hist[b_hi] = excl;
+  hist[b_lo] = excl + c_hi;
+  __syncthreads();
+
+  // 4. scatter
+  for (int t = tid; t < n_tiles; t += kPlanThreads) {
+    const int s = find_segment(seg_off, nseg, t);
+    const int row0 = (t - seg_off[s]) * a.rows;
+    const int pos = atomicAdd(&hist[tile_bucket(a, s, row0)], 1);
+    a.ws.tiles[pos] = make_int2(s, row0);
+  }
+  __syncthreads();
+
+  if (tid == 0) {
+    a.ws.header->n_tiles = n_tiles;
+    a.ws.header->err = s_err;
+    a.ws.header->key = a.key;
+    a.ws.header->rows_per_tile = a.rows;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gvattn

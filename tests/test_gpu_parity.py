@@ -1,0 +1,312 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle.
+
+Small seeded geometries are compared element by element on every used row;
+the full-size workloads are compared on sampled segments / rows that the
+oracle computes one by one, plus whole-buffer properties (gap rows bit-exact,
+-inf / zero rows, finiteness).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from segmented_varlen_attention_amd import binding as B
+from segmented_varlen_attention_amd import workloads as W
+
+from gpu_util import (DeviceCase, check_gap_rows, compare, compare_full, compare_sampled, i32,
+                      oracle_abs, say, to_np, torch, used_row_mask)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load_library()
+    yield
+
+
+# --- small sweeps: every used row ---------------------------------------------
+
+EDGE_Q = [0, 1, 31, 32, 33, 70, 96]
+EDGE_K = [0, 1, 63, 64, 65, 129, 160]
+
+
+def small_case(seed, g, d, causal, dtype, hkv=2):
+    rng = np.random.default_rng(seed)
+    nseg = 7
+    uq = rng.permutation(EDGE_Q)[:nseg]
+    uk = rng.permutation(EDGE_K)[:nseg]
+    return W.random_small(seed, nseg, 96, 160, g * hkv, hkv, d, causal, dtype,
+                          lengths=(uq, uk))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("g", [1, 2, 3, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_bf16(d, g, causal):
+    wl = small_case(100 + d + g, g, d, causal, W.BF16)
+    say(f"[small bf16] d={d} g={g} causal={causal} uq={wl.geom.used_q} uk={wl.geom.used_k}")
+    dc = DeviceCase(wl)
+    out, lse, _ = dc.fwd()
+    st = compare_full(out, lse, wl, where=f"bf16 d{d} g{g} c{int(causal)}", derived=True)
+    say("   ", st)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_fp32(d, causal):
+    wl = small_case(200 + d, 3, d, causal, W.FP32)
+    say(f"[small fp32] d={d} causal={causal}")
+    dc = DeviceCase(wl)
+    out, lse, _ = dc.fwd()
+    say("   ", compare_full(out, lse, wl, where=f"fp32 d{d} c{int(causal)}"))
+
+
+def test_many_segments_tiny_lengths():
+    """1000 segments of capacity <= 5: many empty and one-row tiles."""
+    rng = np.random.default_rng(7)
+    nseg = 1000
+    caps_q = rng.integers(0, 6, nseg)
+    caps_k = rng.integers(0, 6, nseg)
+    uq = np.array([rng.integers(0, c + 1) for c in caps_q])
+    uk = np.array([rng.integers(0, c + 1) for c in caps_k])
+    g = W.make_geometry(caps_q, caps_k, uq, uk, 8, 2, 128, causal=True)
+    q, k, v = W.fill_qkv(g, 8)
+    wl = W.Workload("tiny_many", 7, g, q, k, v)
+    out, lse, _ = DeviceCase(wl).fwd()
+    say("[many tiny]", compare_full(out, lse, wl, where="many tiny", derived=True))
+
+
+# --- the five workloads -------------------------------------------------------------
+
+def test_config1_fp32():
+    wl = W.config1()
+    out, lse, _ = DeviceCase(wl).fwd()
+    st = compare_full(out, lse, wl, where="config1")
+    say("[config1]", st)
+    lse_np = to_np(lse)
+    g = wl.geom
+    rows = slice(g.cu_q[1], g.cu_q[1] + g.used_q[1])  # the segment with no keys
+    assert np.all(np.isneginf(lse_np[:, rows])) and np.all(to_np(out)[rows] == 0.0)
+
+
+def test_config2_cfg_cross_attention():
+    wl = W.config2()
+    g = wl.geom
+    dc = DeviceCase(wl)
+    out, lse, _ = dc.fwd()
+    o_ref, l_ref = oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                                        float(g.scale), False, workers=16)
+    st = compare_full(out, lse, wl, o_ref=o_ref, l_ref=l_ref, where="config2")
+    say("[config2]", st)
+    # equals attention over the text trimmed per sample, not the unmasked form
+    lens = [int(x) for x in g.used_k]
+    keep = np.concatenate([np.arange(g.cu_k[s], g.cu_k[s] + L) for s, L in enumerate(lens)])
+    cu_t = np.array([0, lens[0], lens[0] + lens[1]])
+    o_t, l_t = oracle.attention_fwd(wl.q, wl.k[keep], wl.v[keep], g.cu_q, cu_t, g.used_q, lens,
+                                    float(g.scale), False, workers=16)
+    o_gpu, l_gpu = to_np(out), to_np(lse)
+    compare(o_gpu, l_gpu, o_t, l_t, True, "config2 vs trimmed")
+    # the unmasked (buggy) result differs measurably for the short sample
+    gb = g.with_keys(g.cu_k, [4096, 4096])
+    ob, lb = oracle.attention_fwd(wl.q[:4096], wl.k[:4096], wl.v[:4096], g.cu_q[:2],
+                                  g.cu_k[:2], g.used_q[:1], gb.used_k[:1], float(g.scale), False,
+                                  workers=16)
+    assert np.max(np.abs(l_gpu[:, :4096] - lb)) > 1.0
+
+
+def test_config3_causal_replay():
+    wl = W.config3()
+    g = wl.geom
+    out, lse, ws = DeviceCase(wl).fwd()
+    assert B.gvattn_read_device_error(ws) == 0
+    empty = [int(s) for s in np.where(g.used_k == 0)[0]]
+    big = [int(s) for s in np.argsort(-(g.used_q.astype(np.int64) * g.used_k))[:3]]
+    more = [s for s in (5, 17, 33, 48, 63) if s not in big + empty]
+    samples = [(s, np.arange(g.used_q[s])) for s in empty + big + more]
+    st = compare_sampled(out, lse, wl, samples, where="config3")
+    say("[config3]", st)
+    # any size: all used rows finite; rows with no visible key exactly (0, -inf)
+    m = used_row_mask(g)
+    t = torch()
+    mt = t.from_numpy(m).to("cuda")
+    assert t.isfinite(out[mt]).all().item()
+    for s in range(g.nseg):
+        uq, uk = int(g.used_q[s]), int(g.used_k[s])
+        n_dead = uq if uk == 0 else max(0, uq - uk)
+        if n_dead:
+            r0 = int(g.cu_q[s])
+            blk = lse[:, r0:r0 + n_dead]
+            assert t.isneginf(blk).all().item(), s
+            assert (out[r0:r0 + n_dead] == 0).all().item(), s
+
+
+def test_config4_partitions_merge():
+    wl = W.config4()
+    g = wl.geom
+    dc = DeviceCase(wl)
+    (cu_a, used_a), (cu_b, used_b) = wl.partitions
+    ga, gb = g.with_keys(cu_a, used_a), g.with_keys(cu_b, used_b)
+    out_a, lse_a, _ = dc.fwd(ga)
+    out_b, lse_b, _ = dc.fwd(gb)
+    out_s, lse_s, _ = dc.fwd(g)  # single pass over all keys
+    out_m, lse_m = dc.new_out()
+    err = i32([0])
+    B.gvattn_lse_merge([out_a, out_b], [lse_a, lse_b], dc.cu_q, dc.used_q, out_m, lse_m,
+                       device_error=err)
+    torch().cuda.synchronize()
+    assert int(err.item()) == 0
+    rng = np.random.default_rng(44)
+    samples = [(s, np.sort(rng.choice(8190, 12, replace=False))) for s in range(8)]
+    samples[0] = (0, np.array([0, 1, 8188, 8189]))
+    st_m = compare_sampled(out_m, lse_m, wl, samples, where="config4 merged")
+    st_s = compare_sampled(out_s, lse_s, wl, samples, where="config4 single")
+    say("[config4] merged", st_m, "single", st_s)
+    # partitions against their own oracle
+    st_a = compare_sampled(out_a, lse_a, wl, samples[:3], geom=ga, where="config4 A")
+    say("[config4] A", st_a)
+    # merged vs single pass on the device, all rows
+    t = torch()
+    d_lse = (lse_m - lse_s).abs().max().item()
+    d_out = (out_m.float() - out_s.float()).abs().max().item()
+    say(f"[config4] merged-vs-single max |dLSE|={d_lse:.3g} max |dO|={d_out:.3g}")
+    assert d_lse <= 2e-5 and d_out <= 1.6e-2
+
+
+def test_config5_large_head():
+    wl = W.config5()
+    g = wl.geom
+    out, lse, ws = DeviceCase(wl).fwd()
+    assert B.gvattn_read_device_error(ws) == 0
+    rng = np.random.default_rng(55)
+    samples = []
+    for s in range(g.nseg):
+        uq = int(g.used_q[s])
+        rows = np.unique(np.concatenate([[0, uq - 1], rng.choice(uq, 6, replace=False)]))
+        samples.append((s, rows))
+    st = compare_sampled(out, lse, wl, samples, where="config5")
+    say("[config5]", st)
+
+
+# --- robustness ---------------------------------------------------------------------
+
+def test_nan_gap_rows_and_segment_isolation():
+    wl = small_case(300, 4, 128, True, W.BF16)
+    g = wl.geom
+    out0, lse0, _ = DeviceCase(wl).fwd()
+    q, k, v = wl.q.copy(), wl.k.copy(), wl.v.copy()
+    for s in range(g.nseg):
+        q[g.cu_q[s] + g.used_q[s]:g.cu_q[s + 1]] = np.nan
+        k[g.cu_k[s] + g.used_k[s]:g.cu_k[s + 1]] = np.nan
+        v[g.cu_k[s] + g.used_k[s]:g.cu_k[s + 1]] = np.nan
+    s0 = int(np.argmax(g.used_q))
+    q[g.cu_q[s0]:g.cu_q[s0] + g.used_q[s0]] *= 2.0  # perturb one segment
+    out1, lse1, _ = DeviceCase(wl, q=q, k=k, v=v).fwd()
+    check_gap_rows(out1, lse1, g)
+    t = torch()
+    m = used_row_mask(g)
+    m[g.cu_q[s0]:g.cu_q[s0 + 1]] = False
+    mt = t.from_numpy(m).to("cuda")
+    assert t.equal(out0[mt].view(t.int16), out1[mt].view(t.int16))
+    assert t.equal(lse0[:, mt].view(t.int32), lse1[:, mt].view(t.int32))
+
+
+def test_deterministic():
+    wl = small_case(301, 4, 128, True, W.BF16)
+    dc = DeviceCase(wl)
+    t = torch()
+    a, la, _ = dc.fwd()
+    b, lb, _ = dc.fwd()
+    assert t.equal(a.view(t.int16), b.view(t.int16)) and t.equal(la.view(t.int32), lb.view(t.int32))
+
+
+def test_plan_then_run_and_plan_mismatch():
+    wl = small_case(302, 4, 128, True, W.BF16)
+    g = wl.geom
+    dc = DeviceCase(wl)
+    ws = B.gvattn_fwd_plan(B.GVATTN_BF16, dc.cu_q, i32(g.cu_k), dc.used_q, i32(g.used_k),
+                           g.total_q, g.total_k, g.hq, g.hkv, g.d, g.causal)
+    out1, lse1, _ = dc.fwd(fn=B.gvattn_fwd_run, workspace=ws)
+    out2, lse2, _ = dc.fwd(fn=B.gvattn_fwd_run, workspace=ws)
+    t = torch()
+    assert t.equal(out1.view(t.int16), out2.view(t.int16))
+    compare_full(out1, lse1, wl, where="plan+run")
+    assert B.gvattn_read_device_error(ws) == 0
+    # a plan built for the non-causal problem does not match a causal run
+    ws2 = B.gvattn_fwd_plan(B.GVATTN_BF16, dc.cu_q, i32(g.cu_k), dc.used_q, i32(g.used_k),
+                            g.total_q, g.total_k, g.hq, g.hkv, g.d, False)
+    out3, lse3, _ = dc.fwd(fn=B.gvattn_fwd_run, workspace=ws2)
+    assert B.gvattn_read_device_error(ws2) & B.GVATTN_DEVERR_PLAN
+    assert (out3.float() == W.SENTINEL).all().item() and (lse3 == W.SENTINEL).all().item()
+
+
+def test_device_errors_skip_bad_segments():
+    wl = small_case(303, 2, 64, False, W.BF16)
+    g = wl.geom
+    dc = DeviceCase(wl)
+    bad = int(np.argmax(g.used_q))
+    used_q = g.used_q.copy()
+    used_q[bad] = (g.cu_q[bad + 1] - g.cu_q[bad]) + 5  # beyond its capacity
+    dc.used_q = i32(used_q)
+    out, lse, ws = dc.fwd()
+    assert B.gvattn_read_device_error(ws) == B.GVATTN_DEVERR_USED_Q
+    rows = slice(g.cu_q[bad], g.cu_q[bad + 1])
+    assert (out[rows].float() == W.SENTINEL).all().item()
+    dc.used_q = i32(g.used_q)
+    good = [s for s in range(g.nseg) if s != bad]
+    compare_sampled(out, lse, wl, [(s, np.arange(g.used_q[s])) for s in good], where="errs")
+    # overlapping capacities reject the whole plan
+    cu_q = g.cu_q.copy()
+    cu_q[2] = cu_q[1] - 10
+    dc.cu_q = i32(cu_q)
+    _, _, ws = dc.fwd()
+    assert B.gvattn_read_device_error(ws) & B.GVATTN_DEVERR_OFFSETS
+
+
+@pytest.mark.parametrize("pdt,odt", [("bf16", "bf16"), ("fp32", "fp32"), ("fp32", "bf16")])
+def test_merge_small(pdt, odt):
+    """Three key partitions (one of them empty for some segments) merged on
+    the device.  The merge kernel itself is held to FP32 accuracy against
+    the oracle merge of the very partials it was given; end to end, the
+    merged result matches the single-pass oracle within the derived bound
+    (the partials were rounded to bf16 once more).  The output may alias
+    partial 0."""
+    t = torch()
+    wl = W.random_small(400, 5, 48, 90, 8, 2, 128, False, W.BF16,
+                        lengths=([48, 0, 17, 33, 48], [90, 40, 0, 7, 61]))
+    g = wl.geom
+    dc = DeviceCase(wl)
+    cuts = []
+    for frac in (0.0, 0.3, 0.7, 1.0):
+        cuts.append([int(round(frac * u)) for u in g.used_k])
+    outs, lses = [], []
+    for p in range(3):
+        cu = np.array([g.cu_k[s] + cuts[p][s] for s in range(g.nseg)] + [g.total_k], np.int32)
+        used = np.array([cuts[p + 1][s] - cuts[p][s] for s in range(g.nseg)], np.int32)
+        o, l, _ = dc.fwd(g.with_keys(cu, used))
+        outs.append(o.float() if pdt == "fp32" else o)
+        lses.append(l)
+    part_o = [to_np(o).astype(np.float64) for o in outs]
+    part_l = [to_np(l).astype(np.float64) for l in lses]
+    om_ref, lm_ref = oracle.lse_merge(part_o, part_l, g.cu_q, g.used_q)
+    o_ref, l_ref = oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                                        float(g.scale), False)
+    if odt == pdt:
+        out, lse = outs[0], lses[0]  # in place
+    else:
+        out = t.full_like(outs[0], W.SENTINEL, dtype=t.bfloat16)
+        lse = t.full_like(lses[0], W.SENTINEL)
+    B.gvattn_lse_merge(outs, lses, dc.cu_q, dc.used_q, out, lse)
+    m = used_row_mask(g)
+    o_gpu, l_gpu = to_np(out), to_np(lse)
+    st = compare(o_gpu[m], l_gpu[:, m], om_ref[m], lm_ref[:, m], odt == "bf16",
+                 f"merge kernel {pdt}->{odt}", tol_out=1e-5)
+    say(f"[merge kernel {pdt}->{odt}]", st)
+    o_abs = oracle_abs(wl)[m]
+    st2 = compare(o_gpu[m], l_gpu[:, m], o_ref[m], l_ref[:, m], True,
+                  f"merge end-to-end {pdt}->{odt}", o_abs=2 * o_abs)
+    say(f"[merge end-to-end {pdt}->{odt}]", st2)
+    check_gap_rows(out, lse, g)
