@@ -7,26 +7,29 @@
 // (GQA folding, FP32 LSE).
 //
 // Design (gfx950):
-//   * A persistent grid walks the plan's tile list (segment, first row),
-//     longest first; work item = (tile, chunk of GF query heads that share
-//     one KV head).  One wave owns 32 query rows of one head.
+//   * A persistent grid walks the plan's tile list (segment, first row);
+//     work item = (tile, chunk of GF query heads sharing one KV head).  One
+//     wave owns 32 query rows of one head, so the K/V tiles in LDS serve
+//     all GF heads of the group.
+//   * K and V tiles (64 keys) move HBM -> LDS with buffer_load ... lds (no
+//     register staging), double-buffered: the loads of tile t+1 run while
+//     tile t is computed, one barrier per tile.  The LDS rows are XOR
+//     swizzled at 16-byte granularity so the matrix-core operand reads are
+//     free of bank conflicts.
 //   * Scores are computed transposed, S^T = K . Q^T, with
-//     v_mfma_f32_32x32x16_bf16: K comes from LDS (row-major), Q stays in
-//     registers for the whole tile.  Each lane then holds 32 of the 64 keys
-//     of one query row, so the row max needs a single cross-lane exchange
-//     and the row sum none until the end.
-//   * The probabilities feed O^T += V^T . P^T directly from the score
-//     registers (no shuffle): V is written to LDS transposed with its keys
-//     permuted inside each 16-key block so every lane reads its 8 keys with
-//     one 16-byte LDS load.
-//   * Online softmax in the exp2 domain, FP32 row max / sum, FP32 LSE.
-//   * Every global access goes through a buffer resource whose size ends
-//     at the segment's last used row: loads past it return zero (ragged key
-//     tiles, gap rows, buffer ends) and stores past it are dropped (gap rows
-//     of O stay bit-exact).  Key-padding and causal masks are applied to the
-//     scores as -inf on boundary tiles only.
-//   * The next K/V tile is prefetched into registers while the current one
-//     is computed; O leaves through LDS so global stores are full rows.
+//     v_mfma_f32_32x32x16_bf16; Q stays in registers.  Each lane then holds
+//     32 of the 64 keys of one query row: one cross-lane exchange per tile
+//     for the row max, none for the row sum until the end.
+//   * O^T += V^T . P^T takes P straight from the score registers; V^T is
+//     read from the row-major V tile with ds_read_b64_tr_b16 (a 4x16
+//     transpose per 16 lanes), so V is never transposed in memory.
+//   * Online softmax in the exp2 domain with FP32 max/sum.  The running max
+//     is only raised (and O rescaled) when a row's max grows by more than
+//     2^8, which keeps the rescale off the common path.
+//   * Buffer resources end at the segment's last used row: loads past it
+//     return zero (ragged key tiles, gap rows, buffer ends) and stores past
+//     it are dropped (gap rows of O stay bit-exact).  Key-padding and causal
+//     masks set scores to -inf on boundary tiles only.
 #include <math.h>
 
 #include "gvattn_internal.h"
@@ -36,44 +39,54 @@ namespace {
 
 using namespace dev;
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 template <int D, int GF, int RB>
 struct Cfg {
   static constexpr int NW = GF * RB;          // waves per workgroup
   static constexpr int NT = 64 * NW;          // threads
   static constexpr int BN = kKeyTile;         // keys per tile
-  static constexpr int KP = D + 8;            // K row pitch in LDS (elements)
-  static constexpr int VP = BN + 8;           // V^T row pitch in LDS
-  static constexpr int OP = D + 8;            // O staging row pitch
-  static constexpr int LDS_KV = BN * KP + D * VP;
-  static constexpr int LDS_O = NW * 32 * OP;
-  static constexpr int LDS = LDS_KV > LDS_O ? LDS_KV : LDS_O;
   static constexpr int CH = D / 8;            // 16-byte chunks per row
-  static constexpr int UNITS = (BN / 4) * CH; // (key quad, chunk) per tile
-  static constexpr int UPT = (UNITS + NT - 1) / NT;
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;        // K + V
+  static constexpr int DMA_PER_TILE = TILE_BYTES / 1024;    // 1 KB per wave instruction
+  static constexpr int OP = D + 8;            // O staging row pitch (elements)
+  static constexpr int O_BYTES = NW * 32 * OP * 2;
+  static constexpr int LDS_BYTES = (2 * STAGE_BYTES > O_BYTES) ? 2 * STAGE_BYTES : O_BYTES;
   static constexpr int KK = D / 16;           // k-steps of the score MFMA
   static constexpr int DB = D / 32;           // 32-wide d blocks of O
+  static constexpr int MIN_BLOCKS = (D <= 128) ? 2 : 1;
+  static constexpr int NDMA = (DMA_PER_TILE + NW - 1) / NW;  // DMA instructions per wave
 };
 
-// Position of key kappa (0..63) inside the V^T row: inside each 16-key
-// block the 4-key quads are stored in the order 0, 2, 1, 3.
-__device__ __forceinline__ int vt_pos(int kappa) {
-  const int blk = kappa >> 4, qd = (kappa >> 2) & 3;
-  const int pq = ((qd & 1) << 1) | (qd >> 1);
-  return (blk << 4) | (pq << 2) | (kappa & 3);
+// XOR swizzles of the 16-byte chunk index inside a row.  K is read as
+// 16 B per lane, 8 consecutive rows per LDS cycle; V is read by
+// ds_read_b64_tr_b16, 4 consecutive rows x 32 B per 16 lanes.
+__device__ __forceinline__ int swz_k(int row) { return row & 7; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(uint32_t lo_src, uint32_t hi_src, int upper) {
-  const uint32_t a = upper ? (lo_src >> 16) : (lo_src & 0xffffu);
-  const uint32_t b = upper ? (hi_src & 0xffff0000u) : (hi_src << 16);
-  return a | b;
+__device__ __forceinline__ i16x4 read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+__device__ __forceinline__ void wait_vmem() {
+  // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 template <int D, int GF, int RB>
-__global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__((Cfg<D, GF, RB>::NT), (Cfg<D, GF, RB>::MIN_BLOCKS))
+void fwd_bf16_kernel(FwdArgs a) {
   using C = Cfg<D, GF, RB>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[C::LDS];
-  __bf16* Ks = lds;
-  __bf16* Vt = lds + C::BN * C::KP;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
   const PlanHeader* hdr = a.ws.header;
   if (hdr->key != a.key) {
@@ -85,7 +98,8 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
   const int64_t n_work = (int64_t)n_tiles * n_hc;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hh = lane >> 5;
   const int hf = wave % GF, rb = wave / GF;
   const int G = a.g.hq / a.g.hkv;
@@ -93,23 +107,48 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
   const uint32_t kstride = (uint32_t)a.g.hkv * D * 2;
   const float c = a.scale_log2;
 
+  // Per-lane global offsets of this wave's K/V DMA instructions: slot s of
+  // a tile (1 KB per instruction, 16 B per lane) holds row s / CH, chunk
+  // (s % CH) ^ swizzle(row).
+  uint32_t koff[C::NDMA], voff[C::NDMA];
+#pragma unroll
+  for (int i = 0; i < C::NDMA; ++i) {
+    const int inst = wave + i * C::NW;
+    const int s = inst * 64 + lane;
+    const int row = s / C::CH, pc = s % C::CH;
+    koff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_k(row)) * 16);
+    voff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_v(row)) * 16);
+  }
+
+  // ds_read_b64_tr_b16 addressing inside each 16-lane group: local lane
+  // i = lane % 16 addresses row 4*hh + i/4 of a 16-key block and the 8 bytes
+  // at element 16*((lane >> 4) & 1) + 4*(i % 4) of a 32-wide d block; lane
+  // i then receives column i (d = db*32 + r32) of those 4 rows.
+  const int il = lane & 15;
+  const int vrow_l = 4 * hh + (il >> 2);
+  const int vd_l = 16 * ((lane >> 4) & 1) + 4 * (il & 3);
+
   for (int64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
     const int t = (int)(w / n_hc);
     const int hc = (int)(w - (int64_t)t * n_hc);
+    // Work-item geometry is wave-uniform: keep it in scalar registers so
+    // the buffer resources built from it need no per-lane loops.
     const int2 tile = a.ws.tiles[t];
-    const int seg = tile.x, row0 = tile.y;
+    const int seg = __builtin_amdgcn_readfirstlane(tile.x);
+    const int row0 = __builtin_amdgcn_readfirstlane(tile.y);
     const int head0 = hc * GF;
     const int head = head0 + hf;
     const int kvh = head0 / G;
-    const int q0 = a.g.cu_q[seg], k0 = a.g.cu_k[seg];
-    const int uq = a.g.used_q[seg], uk = a.g.used_k[seg];
-    const int wr0 = row0 + rb * 32;                 // first row of this wave
+    const int q0 = __builtin_amdgcn_readfirstlane(a.g.cu_q[seg]);
+    const int k0 = __builtin_amdgcn_readfirstlane(a.g.cu_k[seg]);
+    const int uq = __builtin_amdgcn_readfirstlane(a.g.used_q[seg]);
+    const int uk = __builtin_amdgcn_readfirstlane(a.g.used_k[seg]);
+    const int wr0 = row0 + rb * 32;                  // first row of this wave
     const int r_last = min(row0 + 32 * RB, uq) - 1;  // last used row of the tile
     int kend = uk;
     if (a.g.causal) kend = max(0, min(uk, r_last + uk - uq + 1));
     const int n_kt = (kend + C::BN - 1) / C::BN;
 
-    // buffer resources limited to the used rows of this segment/head
     const __bf16* qbase = static_cast<const __bf16*>(a.q) + ((int64_t)q0 * a.g.hq + head) * D;
     const uint32_t qbytes = uq > 0 ? (uint32_t)(uq - 1) * qstride + D * 2 : 0u;
     const auto qr = make_rsrc(qbase, qbytes);
@@ -117,6 +156,21 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
     const uint32_t kbytes = uk > 0 ? (uint32_t)(uk - 1) * kstride + D * 2 : 0u;
     const auto kr = make_rsrc(static_cast<const __bf16*>(a.k) + kvoff, kbytes);
     const auto vr = make_rsrc(static_cast<const __bf16*>(a.v) + kvoff, kbytes);
+
+    auto issue_tile = [&](int kt) {
+      char* st = lds + (kt & 1) * C::STAGE_BYTES;
+      const uint32_t soff = (uint32_t)kt * C::BN * kstride;
+#pragma unroll
+      for (int i = 0; i < C::NDMA; ++i) {
+        const int inst = wave + i * C::NW;
+        if (inst < C::DMA_PER_TILE) {
+          dma16(kr, st + inst * 1024, koff[i], soff);
+          dma16(vr, st + C::TILE_BYTES + inst * 1024, voff[i], soff);
+        }
+      }
+    };
+
+    if (n_kt > 0) issue_tile(0);
 
     // Q fragment: lane holds Q[wr0 + r32][16*kk + 8*hh .. +7]
     bf16x8 qf[C::KK];
@@ -136,60 +190,24 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
     const int lim = a.g.causal ? min(uk, row + uk - uq + 1) : uk;
     const int lim_w = a.g.causal ? min(uk, wr0 + uk - uq + 1) : uk;  // wave minimum
 
-    u32x4 kreg[C::UPT][4], vreg[C::UPT][4];
-    auto gload = [&](int kt) {
-#pragma unroll
-      for (int u = 0; u < C::UPT; ++u) {
-        const int unit = tid + u * C::NT;
-        if (unit < C::UNITS) {
-          const int p = unit / C::CH, ch = unit % C::CH;
-          const uint32_t off = (uint32_t)(kt * C::BN + 4 * p) * kstride + ch * 16;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            kreg[u][r] = buf_load16(kr, off + r * kstride);
-            vreg[u][r] = buf_load16(vr, off + r * kstride);
-          }
-        }
-      }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-      for (int u = 0; u < C::UPT; ++u) {
-        const int unit = tid + u * C::NT;
-        if (unit < C::UNITS) {
-          const int p = unit / C::CH, ch = unit % C::CH;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<u32x4*>(Ks + (4 * p + r) * C::KP + 8 * ch) = kreg[u][r];
-          const int pos = vt_pos(4 * p);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int dw = j >> 1, up = j & 1;
-            u32x2 pr;
-            pr[0] = pack2(vreg[u][0][dw], vreg[u][1][dw], up);
-            pr[1] = pack2(vreg[u][2][dw], vreg[u][3][dw], up);
-            *reinterpret_cast<u32x2*>(Vt + (8 * ch + j) * C::VP + pos) = pr;
-          }
-        }
-      }
-    };
-
-    if (n_kt > 0) gload(0);
     for (int kt = 0; kt < n_kt; ++kt) {
+      wait_vmem();
       __syncthreads();
-      lstore();
-      __syncthreads();
-      if (kt + 1 < n_kt) gload(kt + 1);
+      if (kt + 1 < n_kt) issue_tile(kt + 1);
+      const char* Ks = lds + (kt & 1) * C::STAGE_BYTES;
+      const char* Vs = Ks + C::TILE_BYTES;
 
       // S^T = K . Q^T for two 32-key blocks
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
-        const __bf16* kp = Ks + (kb * 32 + r32) * C::KP + 8 * hh;
+        const int krow = kb * 32 + r32;
+        const char* kp = Ks + krow * (D * 2);
+        const int sw = swz_k(krow);
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + (((2 * kk + hh) ^ sw) << 4));
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[kb], 0, 0, 0);
         }
       }
@@ -206,17 +224,23 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
           }
       }
 
-      // online softmax (exp2 domain)
+      // online softmax (exp2 domain), running max raised lazily
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
       mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
+      const float cand = mx * c;
+      if (__any(cand > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, cand);
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -226,11 +250,7 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
           s[kb][v] = p;
           rs += p;
         }
-      l_run = l_run * alpha + rs;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
-      }
+      l_run += rs;
 
       // P^T as bf16 MFMA operands straight from the score registers
       bf16x8 pb[2][2];
@@ -241,15 +261,21 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
 #pragma unroll
           for (int j = 0; j < 8; ++j) pb[kb][a2][j] = (__bf16)s[kb][8 * a2 + j];
 
-      // O^T += V^T . P^T
+      // O^T += V^T . P^T, V^T read transposed from the row-major V tile
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const __bf16* vp = Vt + (db * 32 + r32) * C::VP + 8 * hh;
+        const int dcol = db * 32 + vd_l;
+        const int ch = dcol >> 3, within = (dcol & 7) * 2;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int a2 = 0; a2 < 2; ++a2) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + kb * 32 + a2 * 16);
+            const int r_lo = kb * 32 + a2 * 16 + vrow_l;
+            const int r_hi = r_lo + 8;
+            const i16x4 lo = read_tr(Vs + r_lo * (D * 2) + ((ch ^ swz_v(r_lo)) << 4) + within);
+            const i16x4 hi = read_tr(Vs + r_hi * (D * 2) + ((ch ^ swz_v(r_hi)) << 4) + within);
+            const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 va = __builtin_bit_cast(bf16x8, both);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][a2], o[db], 0, 0, 0);
           }
       }
@@ -263,8 +289,8 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
       const float lse = dead ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
       a.lse[(int64_t)head * a.g.total_q + q0 + row] = lse;
     }
-    __syncthreads();
-    __bf16* Os = lds + wave * 32 * C::OP;
+    __syncthreads();  // every wave is done with the K/V stages
+    __bf16* Os = reinterpret_cast<__bf16*>(lds) + wave * 32 * C::OP;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -286,7 +312,7 @@ __global__ __launch_bounds__((Cfg<D, GF, RB>::NT)) void fwd_bf16_kernel(FwdArgs 
         buf_store16(orr, (uint32_t)(wr0 + r) * qstride + ch * 16, val);
       }
     }
-    __syncthreads();
+    __syncthreads();  // staging area is reused by the next item's K/V loads
   }
 }
 
@@ -295,7 +321,7 @@ hipError_t launch_one(const FwdArgs& a, int64_t max_work, hipStream_t s) {
   using C = Cfg<D, GF, RB>;
   auto kern = fwd_bf16_kernel<D, GF, RB>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), C::NT, max_work);
-  if (grid <= 0) return hipSuccess;
+  if (grid <= 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, s, a);
   return hipGetLastError();
 }

@@ -7,8 +7,10 @@ which alone reaches 7.8e-3 where |O| >= 2); fp32 output <= 1e-5; LSE
 max-abs <= 1e-5; gap rows and the -inf / zero rows exact.
 
 The bf16 path multiplies P, rounded to bf16 (relative error <= 2^-8 per
-weight), by V on the matrix cores, so its error beyond output rounding is
-bounded by 2^-8 * sum_j w_j |v_j| (+ FP32 terms).  On adversarial small
+weight), by V on the matrix cores, so before the output is rounded its error
+is e <= 2^-8 * sum_j w_j |v_j| (+ FP32 terms); rounding the output can then
+flip to the neighbouring bf16 value, so the error beyond |bf16(O_ref) -
+O_ref| is at most 2e = 2^-7 * sum_j w_j |v_j|.  On adversarial small
 sweeps (rows that see a handful of keys with |v| up to 5) that bound exceeds
 5e-3; those tests pass ``o_abs`` = the oracle on |V| and check the derived
 bound instead, while the named workloads keep the flat 5e-3."""
@@ -115,14 +117,14 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return W.round_to_bf16(np.asarray(x, np.float32)).astype(np.float64)
 
 
-P_ROUND = 2.0 ** -8
+P_ROUND = 2.0 ** -7
 
 
 def compare(o_gpu, l_gpu, o_ref, l_ref, bf16: bool, where: str = "", o_abs=None,
             tol_out=None) -> dict:
     """o_* [n, hq, dv], l_* [hq, n] for the same used rows.  ``o_abs`` (the
     oracle run on |V|) switches the bf16 bound to the derived
-    max(5e-3, 2^-8 * o_abs + 1e-5); ``tol_out`` overrides the flat bound."""
+    max(5e-3, 2^-7 * o_abs + 1e-5); ``tol_out`` overrides the flat bound."""
     dead = np.isneginf(l_ref)
     assert np.array_equal(np.isneginf(l_gpu), dead), f"{where}: -inf LSE rows differ"
     dead_rows = dead.T  # [n, hq]
