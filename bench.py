@@ -67,21 +67,25 @@ def algorithmic_bytes(geom, elem=2) -> int:
             + uk * geom.hkv * geom.d * elem * 2)
 
 
-def cpu_baseline(wl, flops_fn, budget_segments: int):
-    """The oracle, as it stands, on a bounded sample of the workload."""
+def cpu_baseline(wl, flops_fn, seconds: float):
+    """The oracle, as it stands, on the same workload: whole passes over all
+    segments, repeated until about ``seconds`` of CPU work have run."""
     import oracle
     g = wl.geom
-    order = [s for s in range(g.nseg) if g.used_q[s] > 0][:budget_segments]
     workers = oracle.host_cores()
-    t0 = time.perf_counter()
-    oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k, float(g.scale),
-                         g.causal, workers=workers, segments=order)
-    dt = time.perf_counter() - t0
-    fl = flops_fn(g.used_q[order], g.used_k[order])
+    passes, dt = 0, 0.0
+    while dt < seconds and passes < 20:
+        t0 = time.perf_counter()
+        oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                             float(g.scale), g.causal, workers=workers)
+        dt += time.perf_counter() - t0
+        passes += 1
+    fl = flops_fn(g.used_q, g.used_k) * passes
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
             "kind": "oracle",
-            "sample": f"segments {order[0]}..{order[-1]} ({len(order)} of {g.nseg}), all "
-                      f"{g.hq} heads, {fl / 1e9:.1f} GFLOP in {dt:.1f} s, FP64 NumPy"}
+            "sample": f"{passes} full pass(es) over all {g.nseg} segments and {g.hq} heads of "
+                      f"the same workload, {fl / 1e9:.1f} GFLOP in {dt:.1f} s, FP64 NumPy, "
+                      f"{workers} worker threads"}
 
 
 def main():
@@ -91,7 +95,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-segments", type=int, default=24)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times), the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -110,6 +117,16 @@ def main():
     gv.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
 
     t0 = time.time()
     wl = W.CONFIGS[args.config]()
@@ -214,7 +231,7 @@ def main():
     }
     if not args.no_cpu_baseline and args.config == 3:
         log("[bench] timing the oracle on a bounded sample ...")
-        res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_segments)
+        res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -73,9 +73,29 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
 }
 
+// v_permlane32_swap with both operands equal leaves lanes 0-31 of the
+// first result and lanes 32-63 of the second holding the lower half's
+// value, and the other two halves holding the upper half's value.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 __device__ __forceinline__ i16x4 read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
 }
+
+// An empty volatile asm statement cannot be speculated, so a branch that
+// contains one stays a branch instead of being if-converted into code that
+// runs on every tile.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
 __device__ __forceinline__ void wait_vmem() {
   // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima
@@ -95,7 +115,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
   const int n_tiles = hdr->n_tiles;
   const int n_hc = a.n_head_chunks;
-  const int64_t n_work = (int64_t)n_tiles * n_hc;
+  const int n_work = n_tiles * n_hc;  // < 2^31: tiles <= total_q / 32 + nseg
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,9 +148,9 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int vrow_l = 4 * hh + (il >> 2);
   const int vd_l = 16 * ((lane >> 4) & 1) + 4 * (il & 3);
 
-  for (int64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int t = (int)(w / n_hc);
-    const int hc = (int)(w - (int64_t)t * n_hc);
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+    const int t = (int)((uint32_t)w / (uint32_t)n_hc);
+    const int hc = w - t * n_hc;
     // Work-item geometry is wave-uniform: keep it in scalar registers so
     // the buffer resources built from it need no per-lane loops.
     const int2 tile = a.ws.tiles[t];
@@ -215,13 +235,15 @@ void fwd_bf16_kernel(FwdArgs a) {
       // key-padding / causal mask on boundary tiles
       const int kbase = kt * C::BN;
       if (kbase + C::BN > lim_w) {
+        // score (kb, v) is key kbase + kb*32 + 8*(v/4) + 4*hh + v%4: it is
+        // masked when its compile-time offset reaches lim - kbase - 4*hh
+        int nv = lim - kbase - 4 * hh;
+        asm volatile("" : "+v"(nv));  // defined here: the compares stay in the branch
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = kbase + kb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (key >= lim) s[kb][v] = -INFINITY;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (kb * 32 + 8 * (v >> 2) + (v & 3) >= nv) s[kb][v] = -INFINITY;
       }
 
       // online softmax (exp2 domain), running max raised lazily
@@ -230,9 +252,10 @@ void fwd_bf16_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = fmaxf(mx, max_across_halves(mx));
       const float cand = mx * c;
       if (__any(cand > m_run + 8.f)) {
+        keep_branch();
         const float m_new = fmaxf(m_run, cand);
         const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
         m_run = m_new;
@@ -282,7 +305,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
 
     // epilogue: normalise, LSE, stage O through LDS, full-row stores
-    const float l_tot = l_run + swap_halves(l_run);
+    const float l_tot = sum_across_halves(l_run);
     const bool dead = (l_tot == 0.f);
     const float inv = dead ? 0.f : 1.f / l_tot;
     if (hh == 0 && row < uq) {
@@ -297,7 +320,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       for (int a4 = 0; a4 < 4; ++a4) {
         bf16x4 ov;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) ov[cc] = (__bf16)(dead ? 0.f : o[db][4 * a4 + cc] * inv);
+        for (int cc = 0; cc < 4; ++cc) ov[cc] = (__bf16)(o[db][4 * a4 + cc] * inv);
         *reinterpret_cast<bf16x4*>(Os + r32 * C::OP + db * 32 + 8 * a4 + 4 * hh) = ov;
       }
     __syncthreads();
