@@ -61,7 +61,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     with _lock:
         if _lib is not None and path is None:
             return _lib
-        p = path or LIB_PATH
+        p = path or os.environ.get("GVATTN_LIBRARY") or LIB_PATH
         if not os.path.exists(p):
             raise RuntimeError(
                 f"libgvattn.so is not built ({p} missing); run "

@@ -62,11 +62,23 @@ struct Cfg {
   static constexpr int NDMA = (DMA_PER_TILE + NW - 1) / NW;  // DMA instructions per wave
 };
 
-// XOR swizzles of the 16-byte chunk index inside a row.  K is read as
-// 16 B per lane, 8 consecutive rows per LDS cycle; V is read by
-// ds_read_b64_tr_b16, 4 consecutive rows x 32 B per 16 lanes.
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
+// XOR swizzles of the 16-byte chunk index inside a row, chosen so that the
+// operand reads are free of bank conflicts on the 64 banks x 4 bytes of the
+// gfx950 LDS (256 bytes per clock).
+//  * K is read 16 bytes per lane, lanes = 16 consecutive rows at one logical
+//    chunk per clock: the 16 rows must land on 16 distinct 16-byte slots of
+//    the 256-byte bank window.
+//  * V is read by ds_read_b64_tr_b16: 32 lanes = 4 consecutive rows x 64
+//    bytes (one 32-wide d block) per clock: the four 64-byte groups must land
+//    in distinct quarters of the window.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return (D == 64) ? ((row >> 1) & 7) : (row & 15);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return (D == 64) ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
+}
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff,
                                       uint32_t soff) {
@@ -136,8 +148,8 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int inst = wave + i * C::NW;
     const int s = inst * 64 + lane;
     const int row = s / C::CH, pc = s % C::CH;
-    koff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_k(row)) * 16);
-    voff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_v(row)) * 16);
+    koff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_k<D>(row)) * 16);
+    voff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_v<D>(row)) * 16);
   }
 
   // ds_read_b64_tr_b16 addressing inside each 16-lane group: local lane
@@ -213,9 +225,26 @@ void fwd_bf16_kernel(FwdArgs a) {
     for (int kt = 0; kt < n_kt; ++kt) {
       wait_vmem();
       __syncthreads();
-      if (kt + 1 < n_kt) issue_tile(kt + 1);
       const char* Ks = lds + (kt & 1) * C::STAGE_BYTES;
       const char* Vs = Ks + C::TILE_BYTES;
+
+      // The loads of tile kt + 1 are spread between the score MFMAs, so
+      // their issue overlaps matrix-core work.  Without a next tile they go
+      // through zero-size buffer resources (every load returns zero into the
+      // stage nobody reads any more), which keeps the phase branch-free.
+      const uint32_t nbytes = (kt + 1 < n_kt) ? kbytes : 0u;
+      const auto krn = make_rsrc(static_cast<const __bf16*>(a.k) + kvoff, nbytes);
+      const auto vrn = make_rsrc(static_cast<const __bf16*>(a.v) + kvoff, nbytes);
+      char* stn = lds + ((kt + 1) & 1) * C::STAGE_BYTES;
+      const uint32_t soffn = (uint32_t)(kt + 1) * C::BN * kstride;
+      auto issue_one = [&](int j) {
+        const int i = j % C::NDMA, which = j / C::NDMA;
+        const int inst = wave + i * C::NW;
+        if (i + 1 < C::NDMA || inst < C::DMA_PER_TILE) {
+          if (which == 0) dma16(krn, stn + inst * 1024, koff[i], soffn);
+          else dma16(vrn, stn + C::TILE_BYTES + inst * 1024, voff[i], soffn);
+        }
+      };
 
       // S^T = K . Q^T for two 32-key blocks
       f32x16 s[2];
@@ -224,11 +253,15 @@ void fwd_bf16_kernel(FwdArgs a) {
         s[kb] = f32x16{};
         const int krow = kb * 32 + r32;
         const char* kp = Ks + krow * (D * 2);
-        const int sw = swz_k(krow);
+        const int sw = swz_k<D>(krow);
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + (((2 * kk + hh) ^ sw) << 4));
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[kb], 0, 0, 0);
+          const int step = kb * C::KK + kk;
+#pragma unroll
+          for (int j = 0; j < 2 * C::NDMA; ++j)
+            if ((j * 2 * C::KK) / (2 * C::NDMA) == step) issue_one(j);
         }
       }
 
@@ -295,8 +328,8 @@ void fwd_bf16_kernel(FwdArgs a) {
           for (int a2 = 0; a2 < 2; ++a2) {
             const int r_lo = kb * 32 + a2 * 16 + vrow_l;
             const int r_hi = r_lo + 8;
-            const i16x4 lo = read_tr(Vs + r_lo * (D * 2) + ((ch ^ swz_v(r_lo)) << 4) + within);
-            const i16x4 hi = read_tr(Vs + r_hi * (D * 2) + ((ch ^ swz_v(r_hi)) << 4) + within);
+            const i16x4 lo = read_tr(Vs + r_lo * (D * 2) + ((ch ^ swz_v<D>(r_lo)) << 4) + within);
+            const i16x4 hi = read_tr(Vs + r_hi * (D * 2) + ((ch ^ swz_v<D>(r_hi)) << 4) + within);
             const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             const bf16x8 va = __builtin_bit_cast(bf16x8, both);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][a2], o[db], 0, 0, 0);
