@@ -11,15 +11,16 @@
 //     work item = (tile, chunk of GF query heads sharing one KV head).  One
 //     wave owns 32 query rows of one head, so the K/V tiles in LDS serve
 //     all GF heads of the group.
-//   * K and V tiles (64 keys) move HBM -> LDS with buffer_load ... lds (no
-//     register staging), double-buffered: the loads of tile t+1 run while
-//     tile t is computed, one barrier per tile.  The LDS rows are XOR
-//     swizzled at 16-byte granularity so the matrix-core operand reads are
-//     free of bank conflicts.
+//   * K and V tiles (32 keys for d <= 128, which fits three workgroups per
+//     compute unit; 64 keys for d = 256) move HBM -> LDS with
+//     buffer_load ... lds (no register staging), double-buffered: the loads
+//     of tile t+1 are issued between the score MFMAs of tile t, one barrier
+//     per tile.  The LDS rows are XOR swizzled at 16-byte granularity so
+//     that the matrix-core operand reads avoid bank conflicts.
 //   * Scores are computed transposed, S^T = K . Q^T, with
 //     v_mfma_f32_32x32x16_bf16; Q stays in registers.  Each lane then holds
-//     32 of the 64 keys of one query row: one cross-lane exchange per tile
-//     for the row max, none for the row sum until the end.
+//     half of the tile's keys for one query row: one cross-lane exchange per
+//     tile for the row max, none for the row sum until the end.
 //   * O^T += V^T . P^T takes P straight from the score registers; V^T is
 //     read from the row-major V tile with ds_read_b64_tr_b16 (a 4x16
 //     transpose per 16 lanes), so V is never transposed in memory.
@@ -44,11 +45,12 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int D, int GF, int RB>
+template <int D, int GF, int RB, int NKB>
 struct Cfg {
   static constexpr int NW = GF * RB;          // waves per workgroup
   static constexpr int NT = 64 * NW;          // threads
-  static constexpr int BN = kKeyTile;         // keys per tile
+  static constexpr int NKB_ = NKB;            // 32-key blocks per tile (1 or 2)
+  static constexpr int BN = 32 * NKB;         // keys per tile
   static constexpr int CH = D / 8;            // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * D * 2;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;        // K + V
@@ -58,7 +60,7 @@ struct Cfg {
   static constexpr int LDS_BYTES = (2 * STAGE_BYTES > O_BYTES) ? 2 * STAGE_BYTES : O_BYTES;
   static constexpr int KK = D / 16;           // k-steps of the score MFMA
   static constexpr int DB = D / 32;           // 32-wide d blocks of O
-  static constexpr int MIN_BLOCKS = (D <= 128) ? 2 : 1;
+  static constexpr int MIN_BLOCKS = (D <= 128) ? (NKB == 1 ? 3 : 2) : 1;
   static constexpr int NDMA = (DMA_PER_TILE + NW - 1) / NW;  // DMA instructions per wave
 };
 
@@ -114,10 +116,10 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, int GF, int RB>
-__global__ __launch_bounds__((Cfg<D, GF, RB>::NT), (Cfg<D, GF, RB>::MIN_BLOCKS))
+template <int D, int GF, int RB, int NKB>
+__global__ __launch_bounds__((Cfg<D, GF, RB, NKB>::NT), (Cfg<D, GF, RB, NKB>::MIN_BLOCKS))
 void fwd_bf16_kernel(FwdArgs a) {
-  using C = Cfg<D, GF, RB>;
+  using C = Cfg<D, GF, RB, NKB>;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
   const PlanHeader* hdr = a.ws.header;
@@ -160,7 +162,18 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int vrow_l = 4 * hh + (il >> 2);
   const int vd_l = 16 * ((lane >> 4) & 1) + 4 * (il & 3);
 
-  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+  // Static schedule.  Work item w lives in queue w % 8 at position w / 8
+  // (with 8 head chunks, queue = head chunk = KV head, and workgroup b runs
+  // on XCD b % 8 under round-robin dispatch, so one XCD's L2 serves one KV
+  // head).  The n_q workgroups of queue q take its items in rounds, forward
+  // in even rounds and backward in odd ones: with the tile list sorted by
+  // decreasing cost, every workgroup alternates long and short items.
+  const int q = blockIdx.x & 7, qi = blockIdx.x >> 3;
+  const int n_q = ((int)gridDim.x - q + 7) >> 3;
+  for (int r = 0;; ++r) {
+    const int j = r * n_q + ((r & 1) ? n_q - 1 - qi : qi);
+    const int w = j * 8 + q;
+    if (w >= n_work) break;
     const int t = (int)((uint32_t)w / (uint32_t)n_hc);
     const int hc = w - t * n_hc;
     // Work-item geometry is wave-uniform: keep it in scalar registers so
@@ -247,9 +260,9 @@ void fwd_bf16_kernel(FwdArgs a) {
       };
 
       // S^T = K . Q^T for two 32-key blocks
-      f32x16 s[2];
+      f32x16 s[C::NKB_];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < C::NKB_; ++kb) {
         s[kb] = f32x16{};
         const int krow = kb * 32 + r32;
         const char* kp = Ks + krow * (D * 2);
@@ -261,7 +274,7 @@ void fwd_bf16_kernel(FwdArgs a) {
           const int step = kb * C::KK + kk;
 #pragma unroll
           for (int j = 0; j < 2 * C::NDMA; ++j)
-            if ((j * 2 * C::KK) / (2 * C::NDMA) == step) issue_one(j);
+            if ((j * C::NKB_ * C::KK) / (2 * C::NDMA) == step) issue_one(j);
         }
       }
 
@@ -273,7 +286,7 @@ void fwd_bf16_kernel(FwdArgs a) {
         int nv = lim - kbase - 4 * hh;
         asm volatile("" : "+v"(nv));  // defined here: the compares stay in the branch
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < C::NKB_; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (kb * 32 + 8 * (v >> 2) + (v & 3) >= nv) s[kb][v] = -INFINITY;
@@ -282,7 +295,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       // online softmax (exp2 domain), running max raised lazily
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::NKB_; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
       mx = fmaxf(mx, max_across_halves(mx));
@@ -299,7 +312,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::NKB_; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = exp2_fast(__builtin_fmaf(s[kb][v], c, -m_use));
@@ -309,9 +322,9 @@ void fwd_bf16_kernel(FwdArgs a) {
       l_run += rs;
 
       // P^T as bf16 MFMA operands straight from the score registers
-      bf16x8 pb[2][2];
+      bf16x8 pb[C::NKB_][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::NKB_; ++kb)
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
@@ -323,7 +336,7 @@ void fwd_bf16_kernel(FwdArgs a) {
         const int dcol = db * 32 + vd_l;
         const int ch = dcol >> 3, within = (dcol & 7) * 2;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < C::NKB_; ++kb)
 #pragma unroll
           for (int a2 = 0; a2 < 2; ++a2) {
             const int r_lo = kb * 32 + a2 * 16 + vrow_l;
@@ -374,8 +387,9 @@ void fwd_bf16_kernel(FwdArgs a) {
 
 template <int D, int GF, int RB>
 hipError_t launch_one(const FwdArgs& a, int64_t max_work, hipStream_t s) {
-  using C = Cfg<D, GF, RB>;
-  auto kern = fwd_bf16_kernel<D, GF, RB>;
+  constexpr int NKB = (D <= 128) ? 1 : 2;
+  using C = Cfg<D, GF, RB, NKB>;
+  auto kern = fwd_bf16_kernel<D, GF, RB, NKB>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), C::NT, max_work);
   if (grid <= 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, s, a);
