@@ -45,6 +45,20 @@ int persistent_grid(const void* kernel, int threads, int64_t max_work) {
   return (int)(max_work < slots ? max_work : slots);
 }
 
+int device_cu_count() {
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  cache.emplace(dev, cus);
+  return cus;
+}
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -168,12 +168,26 @@ void fwd_bf16_kernel(FwdArgs a) {
   // head).  The n_q workgroups of queue q take its items in rounds, forward
   // in even rounds and backward in odd ones: with the tile list sorted by
   // decreasing cost, every workgroup alternates long and short items.
+  //
+  // Workgroups sharing a compute unit are dispatched in slots (slot =
+  // blockIdx / compute units) and wave arbitration favours the older ones,
+  // so with equal work the last slot would finish well after the first.
+  // The wave priority therefore rotates with every item: each workgroup
+  // holds the top priority for 1 / slots of its items.
   const int q = blockIdx.x & 7, qi = blockIdx.x >> 3;
   const int n_q = ((int)gridDim.x - q + 7) >> 3;
+  const int n_slots = min(4, ((int)gridDim.x + a.n_cu - 1) / a.n_cu);
+  const int slot = (int)blockIdx.x / a.n_cu;
   for (int r = 0;; ++r) {
     const int j = r * n_q + ((r & 1) ? n_q - 1 - qi : qi);
     const int w = j * 8 + q;
     if (w >= n_work) break;
+    switch ((r + slot) % n_slots) {
+      case 0: __builtin_amdgcn_s_setprio(0); break;
+      case 1: __builtin_amdgcn_s_setprio(1); break;
+      case 2: __builtin_amdgcn_s_setprio(2); break;
+      default: __builtin_amdgcn_s_setprio(3); break;
+    }
     const int t = (int)((uint32_t)w / (uint32_t)n_hc);
     const int hc = w - t * n_hc;
     // Work-item geometry is wave-uniform: keep it in scalar registers so
@@ -392,7 +406,10 @@ hipError_t launch_one(const FwdArgs& a, int64_t max_work, hipStream_t s) {
   auto kern = fwd_bf16_kernel<D, GF, RB, NKB>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), C::NT, max_work);
   if (grid <= 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, s, a);
+  FwdArgs args = a;
+  args.n_cu = device_cu_count();
+  if (args.n_cu <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, s, args);
   return hipGetLastError();
 }
 

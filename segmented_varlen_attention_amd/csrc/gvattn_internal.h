@@ -133,6 +133,7 @@ struct FwdArgs {
   float scale_log2;     // softmax_scale * log2(e)
   uint32_t key;
   int32_t n_head_chunks;  // hq / gf
+  int32_t n_cu;           // compute units of the device (set by the launcher)
 };
 
 struct MergeArgs {
@@ -162,6 +163,9 @@ hipError_t launch_merge(const MergeArgs& a, int part_dtype, int out_dtype, hipSt
 // Persistent grid size for a kernel: resident blocks per CU x CUs, capped by
 // the work available.
 int persistent_grid(const void* kernel, int threads, int64_t max_work);
+
+// Compute units of the current device (cached), or -1 on a HIP error.
+int device_cu_count();
 
 }  // namespace gvattn
 
