@@ -8,7 +8,9 @@ over used rows: every visible (query, key) pair costs 4*d FLOPs per query
 head; masked, gap and padding work is never counted.
 
 Prints one JSON line.  ``--config N`` benches another workload (2, 4, 5:
-4 times the two partition launches plus the LSE merge).
+4 times the two partition launches plus the LSE merge); ``--dtype fp16``
+runs the same workload through the fp16 matrix-core path (the bf16-exact
+draws converted to fp16).
 """
 
 from __future__ import annotations
@@ -28,7 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 CSRC = os.path.join(ROOT, "segmented_varlen_attention_amd", "csrc")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_bf16_causal_replay_64x2048_pmc.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_mfma_bf16_causal_replay_64x2048_pmc.md")
 
 
 def log(*a):
@@ -94,6 +96,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -147,7 +150,8 @@ def main():
         return pairs * g.hq * (2 * g.d + 2 * g.dv)
 
     flops = flops_of(g.used_q, g.used_k)
-    tdt = torch.bfloat16
+    tdt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+    dcode = gv.GVATTN_BF16 if args.dtype == "bf16" else gv.GVATTN_FP16
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
     q, k, v = up(wl.q).to(tdt), up(wl.k).to(tdt), up(wl.v).to(tdt)
     cu_q, used_q = up(g.cu_q), up(g.used_q)
@@ -158,12 +162,12 @@ def main():
     if args.config == 4:
         launches = [(up(cu), up(u)) for cu, u in wl.partitions]
         parts = [(torch.empty_like(out), torch.empty_like(lse)) for _ in launches]
-        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, gv.GVATTN_BF16)
+        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode)
                for _ in launches]
     else:
         launches = [(up(g.cu_k), up(g.used_k))]
         parts = [(out, lse)]
-        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, gv.GVATTN_BF16)]
+        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode)]
 
     def step():
         for (cu_k, used_k), (o, l), ws in zip(launches, parts, wss):
@@ -209,7 +213,7 @@ def main():
 
     tflops = flops / (ms * 1e-3) / 1e12
     achieved = kern_flops / (kern_ms * 1e-3) / 1e12
-    traffic_rec = recorded_traffic() if args.config == 3 else None
+    traffic_rec = recorded_traffic() if (args.config == 3 and args.dtype == "bf16") else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": (traffic_rec["bytes_per_launch"] if traffic_rec else None)}
@@ -221,15 +225,16 @@ def main():
         "metric": "gapped varlen attn fwd TFLOP/s (used rows) + % of MI355X bf16 MFMA peak",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": names[args.config], "segments": g.nseg,
+        "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": names[args.config].replace("bf16", args.dtype, 1),
+                   "segments": g.nseg,
                    "used_q_rows": int(np.sum(g.used_q)), "hq": g.hq, "hkv": g.hkv, "d": g.d,
                    "causal": bool(g.causal), "flop_per_step": flops,
                    "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
                    "algorithmic_hbm_bytes": algorithmic_bytes(g)},
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline and args.config == 3:
+    if not args.no_cpu_baseline and args.config == 3 and args.dtype == "bf16":
         log("[bench] timing the oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_seconds)
     print(json.dumps(res), flush=True)

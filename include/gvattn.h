@@ -71,7 +71,8 @@ typedef enum gvattn_status {
 
 typedef enum gvattn_dtype {
   GVATTN_FP32 = 0,
-  GVATTN_BF16 = 1
+  GVATTN_BF16 = 1,
+  GVATTN_FP16 = 2
 } gvattn_dtype;
 
 /* Device error word bits (see gvattn_read_device_error). */
@@ -98,7 +99,9 @@ size_t gvattn_fwd_workspace_size(int32_t nseg, int32_t total_q, int32_t hq,
 /*
  * Segmented varlen attention forward: plan + run (PR #302, "What").
  *
- *   dtype            GVATTN_BF16 (MFMA path) or GVATTN_FP32.
+ *   dtype            GVATTN_BF16 or GVATTN_FP16 (matrix-core path, fp32
+ *                    accumulation, P and O rounded to nearest even) or
+ *                    GVATTN_FP32 (vector path).
  *   q, k, v          device, layouts above; may hold anything (NaN
  *                    included) in gap rows, which are never read into a
  *                    result.
@@ -171,12 +174,14 @@ int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
  *                  [total_q, hq, d] of part_dtype.
  *   part_lse       HOST array of nparts device pointers, each fp32
  *                  [hq, total_q].
- *   part_dtype     element type of the partial outputs.
- *   out_dtype      element type of `out`.
+ *   part_dtype     element type of the partial outputs (any gvattn_dtype).
+ *   out_dtype      element type of `out` (any gvattn_dtype).
  *   cu_seqlens_q   device int32 [nseg + 1]; seqused_q device int32 [nseg].
- *   out, lse       device; may alias part_out[0] / part_lse[0] (each row and
- *                  head is read completely before it is written), no other
- *                  overlap.
+ *   out, lse       device; `out` may be part_out[0] when out_dtype equals
+ *                  part_dtype, and `lse` may be part_lse[0] (each row and
+ *                  head is read completely before it is written); no other
+ *                  overlap.  out == part_out[0] with differing element
+ *                  types is GVATTN_ERR_INVALID_ARG.
  *   device_error   optional device int32; invalid segments are skipped and
  *                  GVATTN_DEVERR_* bits are OR-ed into it.  May be NULL.
  */

@@ -7,6 +7,7 @@ synthetic workloads used by the tests and the benchmark.
 
 from .binding import (  # noqa: F401
     GVATTN_BF16,
+    GVATTN_FP16,
     GVATTN_FP32,
     alloc_workspace,
     gvattn_fwd,

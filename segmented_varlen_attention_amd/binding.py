@@ -23,6 +23,7 @@ GVATTN_ERR_HIP = 4
 
 GVATTN_FP32 = 0
 GVATTN_BF16 = 1
+GVATTN_FP16 = 2
 
 GVATTN_DEVERR_USED_Q = 1
 GVATTN_DEVERR_USED_K = 2
@@ -94,9 +95,11 @@ def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.bfloat16:
         return GVATTN_BF16
+    if t.dtype == torch.float16:
+        return GVATTN_FP16
     if t.dtype == torch.float32:
         return GVATTN_FP32
-    raise ValueError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    raise ValueError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
 def _stream_ptr(stream) -> int:

@@ -25,7 +25,7 @@ ARCH = os.environ.get("GVATTN_ARCH", "gfx950")
 SOURCES = [
     "gvattn_api.hip",
     "gvattn_plan.hip",
-    "gvattn_fwd_bf16.hip",
+    "gvattn_fwd_mfma.hip",
     "gvattn_fwd_fp32.hip",
     "gvattn_merge.hip",
 ]

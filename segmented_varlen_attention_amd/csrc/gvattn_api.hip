@@ -63,7 +63,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-bool dtype_ok(int32_t dtype) { return dtype == GVATTN_FP32 || dtype == GVATTN_BF16; }
+bool dtype_ok(int32_t dtype) {
+  return dtype == GVATTN_FP32 || dtype == GVATTN_BF16 || dtype == GVATTN_FP16;
+}
 bool dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
 int esize(int32_t dtype) { return dtype == GVATTN_FP32 ? 4 : 2; }
 
@@ -133,7 +135,7 @@ int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   a.n_head_chunks = g.hq / t.gf;
   const int64_t max_work = max_tiles(g.nseg, g.total_q, t.rows) * a.n_head_chunks;
   bool ok = false;
-  hipError_t e = (dtype == GVATTN_BF16) ? launch_fwd_bf16(a, t, max_work, stream, &ok)
+  hipError_t e = (dtype != GVATTN_FP32) ? launch_fwd_mfma(a, dtype, t, max_work, stream, &ok)
                                         : launch_fwd_fp32(a, t, max_work, stream, &ok);
   if (!ok) return GVATTN_ERR_UNSUPPORTED;
   return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
@@ -238,6 +240,7 @@ int gvattn_lse_merge(int32_t nparts, const void* const* part_out, const float* c
     a.part_out[p] = part_out[p];
     a.part_lse[p] = part_lse[p];
   }
+  if (out == part_out[0] && out_dtype != part_dtype) return GVATTN_ERR_INVALID_ARG;
   a.nparts = nparts;
   a.cu_q = cu_q;
   a.used_q = used_q;

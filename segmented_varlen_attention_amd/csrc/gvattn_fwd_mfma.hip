@@ -1,4 +1,4 @@
-// BF16 segmented varlen attention forward on gfx950 matrix cores.
+// BF16 / FP16 segmented varlen attention forward on gfx950 matrix cores.
 //
 // What it computes: cosmos-framework PR #302, "What" (used prefixes of each
 // segment, untouched gap rows, zero output / -inf LSE without keys);
@@ -18,9 +18,9 @@
 //     per tile.  The LDS rows are XOR swizzled at 16-byte granularity so
 //     that the matrix-core operand reads avoid bank conflicts.
 //   * Scores are computed transposed, S^T = K . Q^T, with
-//     v_mfma_f32_32x32x16_bf16; Q stays in registers.  Each lane then holds
-//     half of the tile's keys for one query row: one cross-lane exchange per
-//     tile for the row max, none for the row sum until the end.
+//     v_mfma_f32_32x32x16_bf16 (or _f16); Q stays in registers.  Each lane
+//     then holds half of the tile's keys for one query row: one cross-lane
+//     exchange per tile for the row max, none for the row sum until the end.
 //   * O^T += V^T . P^T takes P straight from the score registers; V^T is
 //     read from the row-major V tile with ds_read_b64_tr_b16 (a 4x16
 //     transpose per 16 lanes), so V is never transposed in memory.
@@ -41,6 +41,26 @@ namespace {
 using namespace dev;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Element type of Q/K/V/O: the matrix-core instruction and the rounding
+// conversions (round to nearest even) for P and O.
+template <typename T> struct Elem;
+template <> struct Elem<__bf16> {
+  using v8 = bf16x8;
+  using v4 = bf16x4;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Elem<_Float16> {
+  using v8 = f16x8;
+  using v4 = f16x4;
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -116,10 +136,13 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, int GF, int RB, int NKB>
+template <typename T, int D, int GF, int RB, int NKB>
 __global__ __launch_bounds__((Cfg<D, GF, RB, NKB>::NT), (Cfg<D, GF, RB, NKB>::MIN_BLOCKS))
-void fwd_bf16_kernel(FwdArgs a) {
+void fwd_mfma_kernel(FwdArgs a) {
   using C = Cfg<D, GF, RB, NKB>;
+  using E = Elem<T>;
+  using v8 = typename E::v8;
+  using v4 = typename E::v4;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
   const PlanHeader* hdr = a.ws.header;
@@ -208,13 +231,13 @@ void fwd_bf16_kernel(FwdArgs a) {
     if (a.g.causal) kend = max(0, min(uk, r_last + uk - uq + 1));
     const int n_kt = (kend + C::BN - 1) / C::BN;
 
-    const __bf16* qbase = static_cast<const __bf16*>(a.q) + ((int64_t)q0 * a.g.hq + head) * D;
+    const T* qbase = static_cast<const T*>(a.q) + ((int64_t)q0 * a.g.hq + head) * D;
     const uint32_t qbytes = uq > 0 ? (uint32_t)(uq - 1) * qstride + D * 2 : 0u;
     const auto qr = make_rsrc(qbase, qbytes);
     const int64_t kvoff = ((int64_t)k0 * a.g.hkv + kvh) * D;
     const uint32_t kbytes = uk > 0 ? (uint32_t)(uk - 1) * kstride + D * 2 : 0u;
-    const auto kr = make_rsrc(static_cast<const __bf16*>(a.k) + kvoff, kbytes);
-    const auto vr = make_rsrc(static_cast<const __bf16*>(a.v) + kvoff, kbytes);
+    const auto kr = make_rsrc(static_cast<const T*>(a.k) + kvoff, kbytes);
+    const auto vr = make_rsrc(static_cast<const T*>(a.v) + kvoff, kbytes);
 
     auto issue_tile = [&](int kt) {
       char* st = lds + (kt & 1) * C::STAGE_BYTES;
@@ -232,12 +255,12 @@ void fwd_bf16_kernel(FwdArgs a) {
     if (n_kt > 0) issue_tile(0);
 
     // Q fragment: lane holds Q[wr0 + r32][16*kk + 8*hh .. +7]
-    bf16x8 qf[C::KK];
+    v8 qf[C::KK];
     {
       const uint32_t roff = (uint32_t)(wr0 + r32) * qstride + hh * 16;
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk)
-        qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(qr, roff + kk * 32));
+        qf[kk] = __builtin_bit_cast(v8, buf_load16(qr, roff + kk * 32));
     }
 
     f32x16 o[C::DB];
@@ -260,8 +283,8 @@ void fwd_bf16_kernel(FwdArgs a) {
       // through zero-size buffer resources (every load returns zero into the
       // stage nobody reads any more), which keeps the phase branch-free.
       const uint32_t nbytes = (kt + 1 < n_kt) ? kbytes : 0u;
-      const auto krn = make_rsrc(static_cast<const __bf16*>(a.k) + kvoff, nbytes);
-      const auto vrn = make_rsrc(static_cast<const __bf16*>(a.v) + kvoff, nbytes);
+      const auto krn = make_rsrc(static_cast<const T*>(a.k) + kvoff, nbytes);
+      const auto vrn = make_rsrc(static_cast<const T*>(a.v) + kvoff, nbytes);
       char* stn = lds + ((kt + 1) & 1) * C::STAGE_BYTES;
       const uint32_t soffn = (uint32_t)(kt + 1) * C::BN * kstride;
       auto issue_one = [&](int j) {
@@ -283,8 +306,8 @@ void fwd_bf16_kernel(FwdArgs a) {
         const int sw = swz_k<D>(krow);
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + (((2 * kk + hh) ^ sw) << 4));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[kb], 0, 0, 0);
+          const v8 ka = *reinterpret_cast<const v8*>(kp + (((2 * kk + hh) ^ sw) << 4));
+          s[kb] = E::mfma(ka, qf[kk], s[kb]);
           const int step = kb * C::KK + kk;
 #pragma unroll
           for (int j = 0; j < 2 * C::NDMA; ++j)
@@ -335,14 +358,14 @@ void fwd_bf16_kernel(FwdArgs a) {
         }
       l_run += rs;
 
-      // P^T as bf16 MFMA operands straight from the score registers
-      bf16x8 pb[C::NKB_][2];
+      // P^T as 16-bit MFMA operands straight from the score registers
+      v8 pb[C::NKB_][2];
 #pragma unroll
       for (int kb = 0; kb < C::NKB_; ++kb)
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pb[kb][a2][j] = (__bf16)s[kb][8 * a2 + j];
+          for (int j = 0; j < 8; ++j) pb[kb][a2][j] = (T)s[kb][8 * a2 + j];
 
       // O^T += V^T . P^T, V^T read transposed from the row-major V tile
 #pragma unroll
@@ -358,8 +381,8 @@ void fwd_bf16_kernel(FwdArgs a) {
             const i16x4 lo = read_tr(Vs + r_lo * (D * 2) + ((ch ^ swz_v<D>(r_lo)) << 4) + within);
             const i16x4 hi = read_tr(Vs + r_hi * (D * 2) + ((ch ^ swz_v<D>(r_hi)) << 4) + within);
             const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 va = __builtin_bit_cast(bf16x8, both);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][a2], o[db], 0, 0, 0);
+            const v8 va = __builtin_bit_cast(v8, both);
+            o[db] = E::mfma(va, pb[kb][a2], o[db]);
           }
       }
     }
@@ -373,19 +396,19 @@ void fwd_bf16_kernel(FwdArgs a) {
       a.lse[(int64_t)head * a.g.total_q + q0 + row] = lse;
     }
     __syncthreads();  // every wave is done with the K/V stages
-    __bf16* Os = reinterpret_cast<__bf16*>(lds) + wave * 32 * C::OP;
+    T* Os = reinterpret_cast<T*>(lds) + wave * 32 * C::OP;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        bf16x4 ov;
+        v4 ov;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) ov[cc] = (__bf16)(o[db][4 * a4 + cc] * inv);
-        *reinterpret_cast<bf16x4*>(Os + r32 * C::OP + db * 32 + 8 * a4 + 4 * hh) = ov;
+        for (int cc = 0; cc < 4; ++cc) ov[cc] = (T)(o[db][4 * a4 + cc] * inv);
+        *reinterpret_cast<v4*>(Os + r32 * C::OP + db * 32 + 8 * a4 + 4 * hh) = ov;
       }
     __syncthreads();
     {
-      __bf16* obase = static_cast<__bf16*>(a.out) + ((int64_t)q0 * a.g.hq + head) * D;
+      T* obase = static_cast<T*>(a.out) + ((int64_t)q0 * a.g.hq + head) * D;
       const auto orr = make_rsrc(obase, qbytes);
 #pragma unroll
       for (int it = 0; it < D / 16; ++it) {
@@ -399,11 +422,11 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int GF, int RB>
+template <typename T, int D, int GF, int RB>
 hipError_t launch_one(const FwdArgs& a, int64_t max_work, hipStream_t s) {
   constexpr int NKB = (D <= 128) ? 1 : 2;
   using C = Cfg<D, GF, RB, NKB>;
-  auto kern = fwd_bf16_kernel<D, GF, RB, NKB>;
+  auto kern = fwd_mfma_kernel<T, D, GF, RB, NKB>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), C::NT, max_work);
   if (grid <= 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
   FwdArgs args = a;
@@ -413,29 +436,38 @@ hipError_t launch_one(const FwdArgs& a, int64_t max_work, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, const TileShape& t, int64_t max_work, hipStream_t s,
                     bool* ok) {
   *ok = true;
   switch (t.gf) {
-    case 4: return launch_one<D, 4, 1>(a, max_work, s);
-    case 3: return launch_one<D, 3, 1>(a, max_work, s);
-    case 2: return launch_one<D, 2, 2>(a, max_work, s);
-    case 1: return launch_one<D, 1, 4>(a, max_work, s);
+    case 4: return launch_one<T, D, 4, 1>(a, max_work, s);
+    case 3: return launch_one<T, D, 3, 1>(a, max_work, s);
+    case 2: return launch_one<T, D, 2, 2>(a, max_work, s);
+    case 1: return launch_one<T, D, 1, 4>(a, max_work, s);
     default: *ok = false; return hipSuccess;
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const FwdArgs& a, const TileShape& t, int64_t max_work, hipStream_t s,
+                    bool* supported) {
+  switch (a.g.d) {
+    case 64: return launch_d<T, 64>(a, t, max_work, s, supported);
+    case 128: return launch_d<T, 128>(a, t, max_work, s, supported);
+    case 256: return launch_d<T, 256>(a, t, max_work, s, supported);
+    default: *supported = false; return hipSuccess;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, const TileShape& t, int64_t max_work,
+hipError_t launch_fwd_mfma(const FwdArgs& a, int dtype, const TileShape& t, int64_t max_work,
                            hipStream_t s, bool* supported) {
-  switch (a.g.d) {
-    case 64: return launch_d<64>(a, t, max_work, s, supported);
-    case 128: return launch_d<128>(a, t, max_work, s, supported);
-    case 256: return launch_d<256>(a, t, max_work, s, supported);
-    default: *supported = false; return hipSuccess;
-  }
+  if (dtype == GVATTN_BF16) return launch_t<__bf16>(a, t, max_work, s, supported);
+  if (dtype == GVATTN_FP16) return launch_t<_Float16>(a, t, max_work, s, supported);
+  *supported = false;
+  return hipSuccess;
 }
 
 }  // namespace gvattn

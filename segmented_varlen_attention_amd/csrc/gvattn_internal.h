@@ -153,7 +153,8 @@ struct MergeArgs {
 
 // Host-side launchers (one translation unit each).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_fwd_bf16(const FwdArgs& a, const TileShape& t, int64_t max_work,
+// Matrix-core forward for 16-bit inputs (dtype GVATTN_BF16 or GVATTN_FP16).
+hipError_t launch_fwd_mfma(const FwdArgs& a, int dtype, const TileShape& t, int64_t max_work,
                            hipStream_t s, bool* supported);
 hipError_t launch_fwd_fp32(const FwdArgs& a, const TileShape& t, int64_t max_work,
                            hipStream_t s, bool* supported);

@@ -39,6 +39,20 @@ template <> struct Vec8<__bf16> {
     *reinterpret_cast<bf16x8*>(p) = o;
   }
 };
+template <> struct Vec8<_Float16> {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ void load(const void* p, float* f) {
+    const f16x8 v = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+  }
+  static __device__ __forceinline__ void store(void* p, const float* f) {
+    f16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (_Float16)f[i];
+    *reinterpret_cast<f16x8*>(p) = o;
+  }
+};
 template <> struct Vec8<float> {
   static __device__ __forceinline__ void load(const void* p, float* f) {
     const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
@@ -181,10 +195,18 @@ hipError_t launch_t(const MergeArgs& a, hipStream_t s, bool* ok) {
 
 hipError_t launch_merge(const MergeArgs& a, int part_dtype, int out_dtype, hipStream_t s,
                         bool* supported) {
-  if (part_dtype == GVATTN_BF16 && out_dtype == GVATTN_BF16) return launch_t<__bf16, __bf16>(a, s, supported);
-  if (part_dtype == GVATTN_BF16 && out_dtype == GVATTN_FP32) return launch_t<__bf16, float>(a, s, supported);
-  if (part_dtype == GVATTN_FP32 && out_dtype == GVATTN_BF16) return launch_t<float, __bf16>(a, s, supported);
-  if (part_dtype == GVATTN_FP32 && out_dtype == GVATTN_FP32) return launch_t<float, float>(a, s, supported);
+  switch (part_dtype * 3 + out_dtype) {
+    case GVATTN_BF16 * 3 + GVATTN_BF16: return launch_t<__bf16, __bf16>(a, s, supported);
+    case GVATTN_BF16 * 3 + GVATTN_FP16: return launch_t<__bf16, _Float16>(a, s, supported);
+    case GVATTN_BF16 * 3 + GVATTN_FP32: return launch_t<__bf16, float>(a, s, supported);
+    case GVATTN_FP16 * 3 + GVATTN_BF16: return launch_t<_Float16, __bf16>(a, s, supported);
+    case GVATTN_FP16 * 3 + GVATTN_FP16: return launch_t<_Float16, _Float16>(a, s, supported);
+    case GVATTN_FP16 * 3 + GVATTN_FP32: return launch_t<_Float16, float>(a, s, supported);
+    case GVATTN_FP32 * 3 + GVATTN_BF16: return launch_t<float, __bf16>(a, s, supported);
+    case GVATTN_FP32 * 3 + GVATTN_FP16: return launch_t<float, _Float16>(a, s, supported);
+    case GVATTN_FP32 * 3 + GVATTN_FP32: return launch_t<float, float>(a, s, supported);
+    default: break;
+  }
   *supported = false;
   return hipSuccess;
 }

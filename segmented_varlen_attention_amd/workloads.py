@@ -11,8 +11,9 @@ Recipe (one seed per workload):
     ``CHUNK`` elements; chunk ``c`` of tensor ``t`` uses its own generator
     ``default_rng([seed, t, c])`` so the values do not depend on how many
     threads fill the tensor;
-  * bf16 workloads round the float32 draws to bf16 with round-to-nearest-even
-    (the values kept in float32 are then exactly representable in bf16);
+  * bf16 and fp16 workloads round the float32 draws to that type with
+    round-to-nearest-even (the values kept in float32 are then exactly
+    representable in it);
   * output and LSE buffers are prefilled with the sentinel 7.0 so untouched
     gap rows can be checked bit for bit.
 
@@ -36,6 +37,7 @@ CHUNK = 1 << 22
 
 FP32 = "fp32"
 BF16 = "bf16"
+FP16 = "fp16"
 
 
 def _pool_threads() -> int:
@@ -63,6 +65,21 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def round_to_fp16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest IEEE binary16 value (ties to even, overflow to
+    infinity), returned as float32."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def round_to(dtype: str, x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the element type ``dtype`` (returned as float32)."""
+    if dtype == BF16:
+        return round_to_bf16(x)
+    if dtype == FP16:
+        return round_to_fp16(x)
+    return np.asarray(x, dtype=np.float32)
+
+
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Upper 16 bits of float32 values that are exactly bf16 (no rounding)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -70,11 +87,11 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def normal_tensor(seed: int, tensor_id: int, shape, std: float = 1.0,
-                  bf16: bool = True, threads: int | None = None) -> np.ndarray:
+                  dtype: str = BF16, threads: int | None = None) -> np.ndarray:
     """Chunked, thread-count independent N(0, std^2) float32 draw.
 
     Each chunk of ``CHUNK`` elements comes from ``default_rng([seed,
-    tensor_id, chunk])``; bf16 workloads round every value to bf16."""
+    tensor_id, chunk])``; every value is then rounded to ``dtype``."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32)
     nchunks = (n + CHUNK - 1) // CHUNK
@@ -85,7 +102,7 @@ def normal_tensor(seed: int, tensor_id: int, shape, std: float = 1.0,
         vals = g.standard_normal(hi - lo, dtype=np.float32)
         if std != 1.0:
             vals *= np.float32(std)
-        out[lo:hi] = round_to_bf16(vals) if bf16 else vals
+        out[lo:hi] = round_to(dtype, vals)
 
     threads = threads or _pool_threads()
     if nchunks <= 1 or threads == 1:
@@ -166,10 +183,10 @@ def make_geometry(caps_q, caps_k, used_q, used_k, hq, hkv, d, causal,
 
 
 def fill_qkv(geom: Geometry, seed: int, std: float = 1.0, threads=None):
-    bf = geom.dtype == BF16
-    q = normal_tensor(seed, 0, (geom.total_q, geom.hq, geom.d), std, bf, threads)
-    k = normal_tensor(seed, 1, (geom.total_k, geom.hkv, geom.d), std, bf, threads)
-    v = normal_tensor(seed, 2, (geom.total_k, geom.hkv, geom.dv), std, bf, threads)
+    dt = geom.dtype
+    q = normal_tensor(seed, 0, (geom.total_q, geom.hq, geom.d), std, dt, threads)
+    k = normal_tensor(seed, 1, (geom.total_k, geom.hkv, geom.d), std, dt, threads)
+    v = normal_tensor(seed, 2, (geom.total_k, geom.hkv, geom.dv), std, dt, threads)
     return q, k, v
 
 

@@ -13,7 +13,13 @@ flip to the neighbouring bf16 value, so the error beyond |bf16(O_ref) -
 O_ref| is at most 2e = 2^-7 * sum_j w_j |v_j|.  On adversarial small
 sweeps (rows that see a handful of keys with |v| up to 5) that bound exceeds
 5e-3; those tests pass ``o_abs`` = the oracle on |V| and check the derived
-bound instead, while the named workloads keep the flat 5e-3."""
+bound instead, while the named workloads keep the flat 5e-3.
+
+fp16 follows the same argument with an 11-bit significand: P rounds with
+relative error <= 2^-11, so the error beyond |fp16(O_ref) - O_ref| is at
+most 2^-10 * sum_j w_j |v_j|; the flat fp16 bar is 1e-3 (fp16 weights below
+2^-14 are subnormal, absolute error <= 2^-25 each, far below it at these
+score spreads)."""
 
 from __future__ import annotations
 
@@ -26,6 +32,7 @@ from segmented_varlen_attention_amd import binding as B
 from segmented_varlen_attention_amd import workloads as W
 
 TOL_BF16 = 5e-3
+TOL_FP16 = 1e-3
 TOL_FP32 = 1e-5
 TOL_LSE = 1e-5
 
@@ -42,7 +49,7 @@ def torch():
 
 def tdtype(geom):
     t = torch()
-    return t.bfloat16 if geom.dtype == W.BF16 else t.float32
+    return {W.BF16: t.bfloat16, W.FP16: t.float16}.get(geom.dtype, t.float32)
 
 
 def upload(x: np.ndarray, geom):
@@ -103,7 +110,7 @@ def check_gap_rows(out, lse, geom):
     t = torch()
     gap = t.from_numpy(~used_row_mask(geom)).to("cuda")
     sent_o = t.tensor(W.SENTINEL, dtype=out.dtype, device="cuda")
-    if out.dtype == t.bfloat16:
+    if out.dtype in (t.bfloat16, t.float16):
         ok_o = (out[gap].view(t.int16) == sent_o.view(t.int16)).all().item()
     else:
         ok_o = (out[gap].view(t.int32) == sent_o.view(t.int32)).all().item()
@@ -113,18 +120,23 @@ def check_gap_rows(out, lse, geom):
     assert ok_l, "gap rows of LSE changed"
 
 
-def bf16_round(x: np.ndarray) -> np.ndarray:
-    return W.round_to_bf16(np.asarray(x, np.float32)).astype(np.float64)
+def out_round(dtype: str, x: np.ndarray) -> np.ndarray:
+    """The exact result rounded to the output element type (float64)."""
+    return W.round_to(dtype, np.asarray(x, np.float32)).astype(np.float64)
 
 
-P_ROUND = 2.0 ** -7
+# Twice the unit roundoff of P's element type, and the flat output bar.
+P_ROUND = {W.BF16: 2.0 ** -7, W.FP16: 2.0 ** -10}
+TOL_OUT = {W.BF16: TOL_BF16, W.FP16: TOL_FP16, W.FP32: TOL_FP32}
 
 
-def compare(o_gpu, l_gpu, o_ref, l_ref, bf16: bool, where: str = "", o_abs=None,
+def compare(o_gpu, l_gpu, o_ref, l_ref, dtype: str, where: str = "", o_abs=None,
             tol_out=None) -> dict:
-    """o_* [n, hq, dv], l_* [hq, n] for the same used rows.  ``o_abs`` (the
-    oracle run on |V|) switches the bf16 bound to the derived
-    max(5e-3, 2^-7 * o_abs + 1e-5); ``tol_out`` overrides the flat bound."""
+    """o_* [n, hq, dv], l_* [hq, n] for the same used rows; ``dtype`` is the
+    output element type.  ``o_abs`` (the oracle run on |V|) switches a 16-bit
+    bound to the derived max(flat, P_ROUND * o_abs + 1e-5); ``tol_out``
+    overrides the flat bound."""
+    bf16 = dtype in (W.BF16, W.FP16)
     dead = np.isneginf(l_ref)
     assert np.array_equal(np.isneginf(l_gpu), dead), f"{where}: -inf LSE rows differ"
     dead_rows = dead.T  # [n, hq]
@@ -136,18 +148,18 @@ def compare(o_gpu, l_gpu, o_ref, l_ref, bf16: bool, where: str = "", o_abs=None,
     err = np.abs(o_gpu.astype(np.float64) - o_ref)
     stats = {"lse_err": lse_err, "out_err": float(err.max(initial=0.0))}
     if bf16:
-        floor = np.abs(bf16_round(o_ref) - o_ref)
+        floor = np.abs(out_round(dtype, o_ref) - o_ref)
         ex = err - floor
         excess = float(np.max(ex, initial=0.0))
         stats.update(out_excess=excess, floor=float(floor.max(initial=0.0)))
-        flat = TOL_BF16 if tol_out is None else tol_out
+        flat = TOL_OUT[dtype] if tol_out is None else tol_out
         if o_abs is None:
-            assert excess <= flat, f"{where}: bf16 output error beyond rounding {excess:.3g} ({stats})"
+            assert excess <= flat, f"{where}: {dtype} output error beyond rounding {excess:.3g} ({stats})"
         else:
-            bound = np.maximum(flat, P_ROUND * o_abs + 1e-5)
-            stats["over_5e-3"] = int(np.count_nonzero(ex > TOL_BF16))
+            bound = np.maximum(flat, P_ROUND[dtype] * o_abs + 1e-5)
+            stats["over_flat"] = int(np.count_nonzero(ex > TOL_OUT[dtype]))
             stats["bound_ratio"] = float(np.max(ex / bound, initial=0.0))
-            assert np.all(ex <= bound), f"{where}: bf16 error beyond derived bound ({stats})"
+            assert np.all(ex <= bound), f"{where}: {dtype} error beyond derived bound ({stats})"
     else:
         flat = TOL_FP32 if tol_out is None else tol_out
         assert stats["out_err"] <= flat, f"{where}: fp32 output error {stats}"
@@ -190,8 +202,8 @@ def compare_full(out, lse, wl, geom=None, o_ref=None, l_ref=None, where="", deri
     check_gap_rows(out, lse, g)
     m = used_row_mask(g)
     o_gpu, l_gpu = to_np(out), to_np(lse)
-    o_abs = oracle_abs(wl, g)[m] if (derived and g.dtype == W.BF16) else None
-    return compare(o_gpu[m], l_gpu[:, m], o_ref[m], l_ref[:, m], g.dtype == W.BF16, where,
+    o_abs = oracle_abs(wl, g)[m] if (derived and g.dtype != W.FP32) else None
+    return compare(o_gpu[m], l_gpu[:, m], o_ref[m], l_ref[:, m], g.dtype, where,
                    o_abs=o_abs)
 
 
@@ -208,6 +220,6 @@ def compare_sampled(out, lse, wl, samples, geom=None, where=""):
         gi = torch().from_numpy(g.cu_q[seg] + rows).to("cuda")
         o_gpu = to_np(out.index_select(0, gi))
         l_gpu = to_np(lse.index_select(1, gi))
-        stats.append(compare(o_gpu, l_gpu, o_ref, l_ref, g.dtype == W.BF16,
+        stats.append(compare(o_gpu, l_gpu, o_ref, l_ref, g.dtype,
                              f"{where} seg {seg}"))
     return {k: max(s[k] for s in stats) for k in stats[0]} if stats else {}

@@ -140,6 +140,10 @@ def test_merge_host_validation(lib):
     assert merge(out=None) == B.GVATTN_ERR_INVALID_ARG
     assert merge(outs=ctypes.cast(one_null, ctypes.c_void_p)) == B.GVATTN_ERR_INVALID_ARG
     assert merge(nseg=0) == B.GVATTN_OK
+    assert merge(pd=B.GVATTN_FP16, od=B.GVATTN_FP32, nseg=0) == B.GVATTN_OK
+    # out may be partial 0 only when both have one element type
+    assert merge(pd=B.GVATTN_FP16, od=B.GVATTN_BF16) == B.GVATTN_ERR_INVALID_ARG
+    assert merge(pd=B.GVATTN_FP32, od=B.GVATTN_FP16) == B.GVATTN_ERR_INVALID_ARG
 
 
 def test_read_device_error_validation(lib):

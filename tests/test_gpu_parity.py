@@ -56,6 +56,19 @@ def test_small_bf16(d, g, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("g", [1, 2, 3, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_fp16(d, g, causal):
+    """Same geometries as the bf16 sweep (other values), fp16 matrix cores."""
+    wl = small_case(150 + d + g, g, d, causal, W.FP16)
+    say(f"[small fp16] d={d} g={g} causal={causal} uq={wl.geom.used_q} uk={wl.geom.used_k}")
+    dc = DeviceCase(wl)
+    out, lse, _ = dc.fwd()
+    st = compare_full(out, lse, wl, where=f"fp16 d{d} g{g} c{int(causal)}", derived=True)
+    say("   ", st)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_small_fp32(d, causal):
     wl = small_case(200 + d, 3, d, causal, W.FP32)
@@ -109,7 +122,7 @@ def test_config2_cfg_cross_attention():
     o_t, l_t = oracle.attention_fwd(wl.q, wl.k[keep], wl.v[keep], g.cu_q, cu_t, g.used_q, lens,
                                     float(g.scale), False, workers=16)
     o_gpu, l_gpu = to_np(out), to_np(lse)
-    compare(o_gpu, l_gpu, o_t, l_t, True, "config2 vs trimmed")
+    compare(o_gpu, l_gpu, o_t, l_t, W.BF16, "config2 vs trimmed")
     # the unmasked (buggy) result differs measurably for the short sample
     gb = g.with_keys(g.cu_k, [4096, 4096])
     ob, lb = oracle.attention_fwd(wl.q[:4096], wl.k[:4096], wl.v[:4096], g.cu_q[:2],
@@ -266,16 +279,19 @@ def test_device_errors_skip_bad_segments():
     assert B.gvattn_read_device_error(ws) & B.GVATTN_DEVERR_OFFSETS
 
 
-@pytest.mark.parametrize("pdt,odt", [("bf16", "bf16"), ("fp32", "fp32"), ("fp32", "bf16")])
+@pytest.mark.parametrize("pdt,odt", [("bf16", "bf16"), ("fp32", "fp32"), ("fp32", "bf16"),
+                                     ("fp16", "fp16"), ("fp16", "fp32"), ("bf16", "fp16")])
 def test_merge_small(pdt, odt):
     """Three key partitions (one of them empty for some segments) merged on
     the device.  The merge kernel itself is held to FP32 accuracy against
     the oracle merge of the very partials it was given; end to end, the
-    merged result matches the single-pass oracle within the derived bound
-    (the partials were rounded to bf16 once more).  The output may alias
-    partial 0."""
+    merged result matches the single-pass oracle within the derived bound of
+    the forward's element type, doubled (the partials were rounded once
+    more).  The output may alias partial 0.  fp32 partials are the bf16
+    forward's outputs widened."""
     t = torch()
-    wl = W.random_small(400, 5, 48, 90, 8, 2, 128, False, W.BF16,
+    fw = W.FP16 if pdt == "fp16" else W.BF16
+    wl = W.random_small(400, 5, 48, 90, 8, 2, 128, False, fw,
                         lengths=([48, 0, 17, 33, 48], [90, 40, 0, 7, 61]))
     g = wl.geom
     dc = DeviceCase(wl)
@@ -297,16 +313,17 @@ def test_merge_small(pdt, odt):
     if odt == pdt:
         out, lse = outs[0], lses[0]  # in place
     else:
-        out = t.full_like(outs[0], W.SENTINEL, dtype=t.bfloat16)
+        odt_t = {"bf16": t.bfloat16, "fp16": t.float16, "fp32": t.float32}[odt]
+        out = t.full_like(outs[0], W.SENTINEL, dtype=odt_t)
         lse = t.full_like(lses[0], W.SENTINEL)
     B.gvattn_lse_merge(outs, lses, dc.cu_q, dc.used_q, out, lse)
     m = used_row_mask(g)
     o_gpu, l_gpu = to_np(out), to_np(lse)
-    st = compare(o_gpu[m], l_gpu[:, m], om_ref[m], lm_ref[:, m], odt == "bf16",
+    st = compare(o_gpu[m], l_gpu[:, m], om_ref[m], lm_ref[:, m], odt,
                  f"merge kernel {pdt}->{odt}", tol_out=1e-5)
     say(f"[merge kernel {pdt}->{odt}]", st)
     o_abs = oracle_abs(wl)[m]
-    st2 = compare(o_gpu[m], l_gpu[:, m], o_ref[m], l_ref[:, m], True,
+    st2 = compare(o_gpu[m], l_gpu[:, m], o_ref[m], l_ref[:, m], fw,
                   f"merge end-to-end {pdt}->{odt}", o_abs=2 * o_abs)
     say(f"[merge end-to-end {pdt}->{odt}]", st2)
     check_gap_rows(out, lse, g)
