@@ -8,9 +8,11 @@ from .gvattn_oracle import (  # noqa: F401
     SCORE_BUDGET_BYTES,
     attention_flops,
     attention_fwd,
+    attention_fwd_ranges,
     bits_equal,
     host_cores,
     lse_merge,
     segment_head_rows,
+    segment_key_rows,
     visible_limit,
 )

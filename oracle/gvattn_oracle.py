@@ -19,6 +19,10 @@ What it computes (the sources are the pages' own statements of the method):
 * cosmos-framework PR #312, "Problem and behavior": GQA folding (several query
   heads share one KV head) and an FP32 LSE merge of the partial results of
   visibility partitions.
+* TensorRT-LLM issue #18687, "Suggested fix" item 1: after the Ulysses
+  all-to-all the keys arrive rank-major, so a sample's valid keys are several
+  runs of rows rather than one prefix.  ``attention_fwd_ranges`` takes each
+  segment's keys as an ordered list of row ranges.
 
 Readings taken where the pages leave a step open:
 
@@ -160,6 +164,63 @@ def attention_fwd(q, k, v, cu_q, cu_k, used_q, used_k, scale, causal,
     return out, lse
 
 
+def segment_key_rows(kr_off, kr_start, kr_len, s: int) -> np.ndarray:
+    """Row indices of segment s's keys: the concatenation, in list order, of
+    its ranges [kr_start[i], kr_start[i] + kr_len[i]) for i in
+    [kr_off[s], kr_off[s + 1])."""
+    parts = [np.arange(int(kr_start[i]), int(kr_start[i]) + int(kr_len[i]), dtype=np.int64)
+             for i in range(int(kr_off[s]), int(kr_off[s + 1]))]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def attention_fwd_ranges(q, k, v, cu_q, used_q, kr_off, kr_start, kr_len, scale, causal,
+                         out_init=None, lse_init=None, workers: int | None = None):
+    """Whole-launch oracle when every segment's keys are a list of row ranges
+    (issue #18687, "Suggested fix" item 1).  The segment's key sequence is the
+    concatenation of its ranges; with it gathered, the computation is the one
+    of ``attention_fwd`` with used_k = the total length (causal alignment is
+    bottom-right over that sequence)."""
+    tq, hq, _ = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    if hq % hkv:
+        raise ValueError(f"hq={hq} is not a multiple of hkv={hkv}")
+    out = (np.zeros((tq, hq, dv)) if out_init is None
+           else np.array(out_init, dtype=np.float64, copy=True))
+    lse = (np.zeros((hq, tq)) if lse_init is None
+           else np.array(lse_init, dtype=np.float64, copy=True))
+    g = hq // hkv
+    items = []
+    for s in range(len(used_q)):
+        uq = int(used_q[s])
+        if uq == 0:
+            continue
+        keys = segment_key_rows(kr_off, kr_start, kr_len, s)
+        for h in range(hq):
+            items.append((s, h, keys))
+
+    def run(item):
+        s, h, keys = item
+        q0, uq, uk = int(cu_q[s]), int(used_q[s]), len(keys)
+        ks, vs = k[keys], v[keys]                        # gathered [uk, Hkv, *]
+        step = max(1, SCORE_BUDGET_BYTES // (max(uk, 1) * 8))
+        for r0 in range(0, uq, step):
+            rows = np.arange(r0, min(uq, r0 + step))
+            o, l = segment_head_rows(q, ks, vs, q0, 0, uq, uk, h, h // g, scale, causal, rows)
+            out[q0 + rows, h, :] = o
+            lse[h, q0 + rows] = l
+
+    workers = workers or host_cores()
+    if workers <= 1 or len(items) <= 1:
+        for it in items:
+            run(it)
+    else:
+        ctx = (_threadpool_limits(limits=1) if _threadpool_limits is not None
+               else _NullCtx())
+        with ctx, _cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(run, items))
+    return out, lse
+
+
 class _NullCtx:
     def __enter__(self):
         return self
@@ -228,6 +289,6 @@ def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
 
 
 __all__ = [
-    "attention_fwd", "lse_merge", "segment_head_rows", "visible_limit",
+    "attention_fwd", "attention_fwd_ranges", "segment_key_rows", "lse_merge", "segment_head_rows", "visible_limit",
     "attention_flops", "host_cores", "bits_equal", "SCORE_BUDGET_BYTES",
 ]

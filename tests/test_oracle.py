@@ -413,3 +413,154 @@ def test_flop_count_config1():
     # causal counts only visible pairs: uq=3, uk=5 -> rows see 3, 4, 5 keys
     assert oracle.attention_flops([3], [5], 1, 1, 1, True) == 12 * 4
     assert oracle.attention_flops([5], [3], 1, 1, 1, True) == 6 * 4
+
+
+# --- key ranges (issue #18687, "Suggested fix" item 1) -------------------------
+
+def brute_force_ranges(q, k, v, cu_q, used_q, kr_off, kr_start, kr_len, scale, causal,
+                       sentinel):
+    """Scalar loops: the segment's key list is built range by range, key by
+    key; key j of that list is visible to row i when, under causal, the
+    list's remaining length after j is at least the row's remaining length
+    in the used queries."""
+    tq, hq, _ = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    group = hq // hkv
+    out = np.full((tq, hq, dv), sentinel)
+    lse = np.full((hq, tq), sentinel)
+    for s in range(len(used_q)):
+        keys = []
+        for i in range(kr_off[s], kr_off[s + 1]):
+            for j in range(kr_len[i]):
+                keys.append(kr_start[i] + j)
+        for i in range(used_q[s]):
+            r = cu_q[s] + i
+            for h in range(hq):
+                kvh = h // group
+                logits, vals = [], []
+                for j, kr in enumerate(keys):
+                    if causal and (len(keys) - 1 - j) < (used_q[s] - 1 - i):
+                        continue
+                    logits.append(scale * math.fsum(float(q[r, h, t]) * float(k[kr, kvh, t])
+                                                    for t in range(q.shape[2])))
+                    vals.append([float(x) for x in v[kr, kvh, :]])
+                if not logits:
+                    out[r, h, :] = 0.0
+                    lse[h, r] = -math.inf
+                    continue
+                w = [math.exp(x) for x in logits]
+                total = math.fsum(w)
+                lse[h, r] = math.log(total)
+                for c in range(dv):
+                    out[r, h, c] = math.fsum(w[j] * vals[j][c] for j in range(len(w))) / total
+    return out, lse
+
+
+@pytest.mark.parametrize("seed,causal", [(61, False), (62, True), (63, True)])
+def test_ranges_brute_force_tiny(seed, causal):
+    """Random ranges: empty ones, overlapping ones, out of order, a segment
+    with no ranges at all."""
+    rng = np.random.default_rng(seed)
+    nseg, hq, hkv, d, tk = 4, 4, 2, 5, 23
+    used_q = np.array([3, 5, 0, 4])
+    cu_q = np.concatenate([[0], np.cumsum(used_q + 1)])
+    counts = [3, 0, 2, 4]
+    kr_off = np.concatenate([[0], np.cumsum(counts)])
+    n = int(kr_off[-1])
+    kr_start = rng.integers(0, tk, n)
+    kr_len = np.array([rng.integers(0, tk - st + 1) for st in kr_start]) // 2
+    kr_len[1] = 0
+    q = rng.standard_normal((int(cu_q[-1]), hq, d)).astype(np.float32)
+    k = rng.standard_normal((tk, hkv, d)).astype(np.float32)
+    v = rng.standard_normal((tk, hkv, d)).astype(np.float32)
+    o_ref, l_ref = brute_force_ranges(q, k, v, cu_q, used_q, kr_off, kr_start, kr_len, 0.41,
+                                      causal, W.SENTINEL)
+    o, l = oracle.attention_fwd_ranges(q, k, v, cu_q, used_q, kr_off, kr_start, kr_len, 0.41,
+                                       causal, np.full_like(o_ref, W.SENTINEL),
+                                       np.full_like(l_ref, W.SENTINEL), workers=1)
+    assert np.array_equal(np.isinf(l), np.isinf(l_ref))
+    fin = np.isfinite(l_ref)
+    assert np.max(np.abs(l[fin] - l_ref[fin]), initial=0) <= 1e-12
+    assert np.max(np.abs(o - o_ref)) <= 1e-12
+    rows = np.concatenate([np.arange(cu_q[s], cu_q[s] + used_q[s]) for s in range(nseg)])
+    assert np.all(l[:, rows[rows >= cu_q[1]][:5]] == -np.inf)  # segment 1 has no ranges
+
+
+def test_ranges_ulysses_rank_major_equals_masked_sdpa(golden):
+    """The issue's layout: two CFG samples, text padded to 8 tokens with real
+    lengths 3 and 7, 12 video tokens, Ulysses size 2.  After the all-to-all
+    the key order is text_r0, video_r0, text_r1, video_r1; the valid keys of
+    a sample are four ranges.  The range form equals SDPA over the full
+    rank-major order with a boolean key mask, the mask-capable backend the
+    issue names as exact."""
+    st = golden["rank_major_keys"]
+    assert st["key_order"] == ["text_r0", "video_r0", "text_r1", "video_r1"]
+    rng = np.random.default_rng(64)
+    ranks, text_cap, video, nq, hq, hkv, d = 2, 8, 12, 10, 4, 2, 8
+    lens = [3, 7]
+    chunk = text_cap // ranks + video // ranks          # rows per rank chunk
+    per_sample = ranks * chunk
+    k = rng.standard_normal((2 * per_sample, hkv, d)).astype(np.float32)
+    v = rng.standard_normal((2 * per_sample, hkv, d)).astype(np.float32)
+    q = rng.standard_normal((2 * nq, hq, d)).astype(np.float32)
+    kr_start, kr_len, masks = [], [], []
+    for b, L in enumerate(lens):
+        base = b * per_sample
+        mask = np.zeros(per_sample, bool)
+        for r in range(ranks):
+            c0 = base + r * chunk
+            real = max(0, min(text_cap // ranks, L - r * (text_cap // ranks)))
+            k[c0 + real:c0 + text_cap // ranks] = 0.0    # pad slots are exact zeros
+            v[c0 + real:c0 + text_cap // ranks] = 0.0
+            kr_start += [c0, c0 + text_cap // ranks]
+            kr_len += [real, video // ranks]
+            mask[r * chunk:r * chunk + real] = True
+            mask[r * chunk + text_cap // ranks:(r + 1) * chunk] = True
+        masks.append(mask)
+    kr_off = np.array([0, 2 * ranks, 4 * ranks])
+    cu_q, used_q = np.array([0, nq, 2 * nq]), np.array([nq, nq])
+    o, l = oracle.attention_fwd_ranges(q, k, v, cu_q, used_q, kr_off, np.array(kr_start),
+                                       np.array(kr_len), 0.35, False, workers=1)
+    for b in range(2):
+        rows = slice(b * nq, (b + 1) * nq)
+        keys = slice(b * per_sample, (b + 1) * per_sample)
+        m = torch.from_numpy(masks[b])[None, None, None, :]
+        ref = _sdpa(q[rows], k[keys], v[keys], 0.35, mask=m)
+        assert np.max(np.abs(o[rows] - ref)) < 1e-12
+        # the unmasked form (pads attended as zeros) differs
+        bad = _sdpa(q[rows], k[keys], v[keys], 0.35)
+        assert np.max(np.abs(bad - ref)) > 1e-3
+
+
+def test_ranges_single_prefix_and_order():
+    """One range per segment, (cu_k, used_k), is the prefix form; without
+    causal the order of a segment's ranges does not matter, with causal it
+    does."""
+    wl = W.random_small(65, nseg=3, cap_q=9, cap_k=14, hq=4, hkv=2, d=8, causal=True,
+                        dtype=W.FP32, lengths=([9, 4, 7], [14, 0, 11]))
+    g = wl.geom
+    kr_off = np.arange(g.nseg + 1)
+    o1, l1 = oracle.attention_fwd_ranges(wl.q, wl.k, wl.v, g.cu_q, g.used_q, kr_off,
+                                         g.cu_k[:-1], g.used_k, float(g.scale), True, workers=1)
+    o2, l2 = run_oracle(wl, out_init=np.zeros_like(o1), lse_init=np.zeros_like(l1))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # split every segment's keys into two ranges, then swap them
+    starts, lens_, off = [], [], [0]
+    for s in range(g.nseg):
+        a = int(g.used_k[s]) // 3
+        starts += [int(g.cu_k[s]) + a, int(g.cu_k[s])]
+        lens_ += [int(g.used_k[s]) - a, a]
+        off.append(len(starts))
+    for causal in (False, True):
+        o3, l3 = oracle.attention_fwd_ranges(wl.q, wl.k, wl.v, g.cu_q, g.used_q, np.array(off),
+                                             np.array(starts), np.array(lens_), float(g.scale),
+                                             causal, workers=1)
+        o4, l4 = oracle.attention_fwd_ranges(wl.q, wl.k, wl.v, g.cu_q, g.used_q, kr_off,
+                                             g.cu_k[:-1], g.used_k, float(g.scale), causal,
+                                             workers=1)
+        if causal:
+            assert np.max(np.abs(o3 - o4)) > 1e-3
+        else:
+            fin = np.isfinite(l4)
+            assert np.array_equal(np.isneginf(l3), np.isneginf(l4))
+            assert np.max(np.abs(o3 - o4)) < 1e-12 and np.max(np.abs(l3[fin] - l4[fin])) < 1e-12
