@@ -8,9 +8,11 @@ over used rows: every visible (query, key) pair costs 4*d FLOPs per query
 head; masked, gap and padding work is never counted.
 
 Prints one JSON line.  ``--config N`` benches another workload (2, 4, 5:
-4 times the two partition launches plus the LSE merge); ``--dtype fp16``
-runs the same workload through the fp16 matrix-core path (the bf16-exact
-draws converted to fp16).
+4 times the two partition launches plus the LSE merge, or with ``--fused``
+one key-range launch over both partitions; 6: the Ulysses rank-major joint
+attention of issue #18687 through the key-range entry point);
+``--dtype fp16`` runs the same workload through the fp16 matrix-core path
+(the bf16-exact draws converted to fp16).
 """
 
 from __future__ import annotations
@@ -61,10 +63,12 @@ def recorded_traffic():
     return None
 
 
-def algorithmic_bytes(geom, elem=2) -> int:
-    """Used Q + used O + LSE + used K + used V, each once."""
+def algorithmic_bytes(geom, elem=2, keys=None) -> int:
+    """Used Q + used O + LSE + used K + used V, each once (``keys``: the
+    per-segment key counts when they are not geom.used_k)."""
     uq = int(np.sum(geom.used_q))
-    uk = int(np.sum(geom.used_k[geom.used_q > 0]))
+    ks = np.asarray(geom.used_k if keys is None else keys)
+    uk = int(np.sum(ks[geom.used_q > 0]))
     return (uq * geom.hq * geom.d * elem * 2 + uq * geom.hq * 4
             + uk * geom.hkv * geom.d * elem * 2)
 
@@ -95,7 +99,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--fused", action="store_true",
+                    help="config 4: both partitions as key ranges of one launch")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -132,8 +138,14 @@ def main():
         return
 
     t0 = time.time()
-    wl = W.CONFIGS[args.config]()
+    wl = W.ulysses_joint() if args.config == 6 else W.CONFIGS[args.config]()
     g = wl.geom
+    fused = args.config == 4 and args.fused
+    if fused:
+        (cu_a, used_a), (cu_b, used_b) = wl.partitions
+        wl.key_ranges = (np.arange(0, 2 * g.nseg + 1, 2, dtype=np.int32),
+                         np.stack([cu_a[:-1], cu_b[:-1]], 1).reshape(-1).astype(np.int32),
+                         np.stack([used_a, used_b], 1).reshape(-1).astype(np.int32))
     log(f"[bench] workload {wl.name} generated in {time.time() - t0:.1f}s")
 
     def flops_of(uq, uk):
@@ -149,7 +161,12 @@ def main():
                 pairs += a * b
         return pairs * g.hq * (2 * g.d + 2 * g.dv)
 
-    flops = flops_of(g.used_q, g.used_k)
+    if wl.key_ranges is not None:
+        kr_lens = [int(np.sum(wl.key_ranges[2][wl.key_ranges[0][s]:wl.key_ranges[0][s + 1]]))
+                   for s in range(g.nseg)]
+        flops = flops_of(g.used_q, kr_lens)
+    else:
+        flops = flops_of(g.used_q, g.used_k)
     tdt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
     dcode = gv.GVATTN_BF16 if args.dtype == "bf16" else gv.GVATTN_FP16
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
@@ -159,7 +176,12 @@ def main():
     lse = torch.full((g.hq, g.total_q), W.SENTINEL, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    if args.config == 4:
+    if wl.key_ranges is not None:
+        kr = tuple(up(x) for x in wl.key_ranges)
+        launches = []
+        parts = [(out, lse)]
+        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode)]
+    elif args.config == 4:
         launches = [(up(cu), up(u)) for cu, u in wl.partitions]
         parts = [(torch.empty_like(out), torch.empty_like(lse)) for _ in launches]
         wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode)
@@ -170,6 +192,10 @@ def main():
         wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode)]
 
     def step():
+        if wl.key_ranges is not None:
+            gv.gvattn_fwd_ranges(q, k, v, cu_q, used_q, *kr, out, lse, float(g.scale), g.causal,
+                                 workspace=wss[0])
+            return
         for (cu_k, used_k), (o, l), ws in zip(launches, parts, wss):
             gv.gvattn_fwd(q, k, v, cu_q, cu_k, used_q, used_k, o, l, float(g.scale), g.causal,
                           workspace=ws)
@@ -178,11 +204,14 @@ def main():
                                 lse)
 
     def run_only():
+        if wl.key_ranges is not None:  # no separate plan: the whole call
+            step()
+            return
         (cu_k, used_k), (o, l), ws = launches[0], parts[0], wss[0]
         gv.gvattn_fwd_run(q, k, v, cu_q, cu_k, used_q, used_k, o, l, float(g.scale), g.causal,
                           ws)
 
-    if args.config == 4:
+    if args.config == 4 and not fused:
         flops = sum(flops_of(g.used_q, u) for _, u in wl.partitions)
 
     for _ in range(args.warmup):
@@ -208,8 +237,28 @@ def main():
     k1.record(stream)
     torch.cuda.synchronize()
     kern_ms = k0.elapsed_time(k1) / args.steps
-    kern_flops = flops_of(g.used_q, launches[0][1].cpu().numpy()) if args.config == 4 else flops
+    kern_flops = (flops_of(g.used_q, launches[0][1].cpu().numpy())
+                  if (args.config == 4 and not fused) else flops)
     log(f"[bench] main kernel alone: {kern_ms:.4f} ms/launch")
+
+    merge_rec = None
+    if args.config == 4 and not fused:
+        # the LSE merge alone: algorithmic bytes = both partials, the output
+        # and the LSEs, used rows only
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pouts, plses = [p[0] for p in parts], [p[1] for p in parts]
+        m0.record(stream)
+        for _ in range(args.steps):
+            gv.gvattn_lse_merge(pouts, plses, cu_q, used_q, out, lse)
+        m1.record(stream)
+        torch.cuda.synchronize()
+        merge_ms = m0.elapsed_time(m1) / args.steps
+        uq = int(np.sum(g.used_q))
+        mbytes = uq * g.hq * (len(parts) * (g.dv * 2 + 4) + g.dv * 2 + 4)
+        merge_rec = {"ms": round(merge_ms, 5), "algorithmic_bytes": mbytes,
+                     "GB_per_s": round(mbytes / (merge_ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(mbytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] LSE merge alone: {merge_ms:.4f} ms, {merge_rec['GB_per_s']} GB/s")
 
     tflops = flops / (ms * 1e-3) / 1e12
     achieved = kern_flops / (kern_ms * 1e-3) / 1e12
@@ -220,20 +269,25 @@ def main():
     names = {2: "bf16_cfg_cross_attn_b2_4096q_text24_700_gqa32x8_d128",
              3: "bf16_causal_gapped_replay_64x2048_gqa32x8_d128",
              4: "bf16_multiview_8x8190q_32760k_2partitions_merge_gqa24x8_d128",
-             5: "bf16_gapped_16x16384_gqa16x4_d256"}
+             5: "bf16_gapped_16x16384_gqa16x4_d256",
+             6: "bf16_ulysses2_rank_major_joint_b2_4096q_text4096_video4096_keyranges"}
     res = {
         "metric": "gapped varlen attn fwd TFLOP/s (used rows) + % of MI355X bf16 MFMA peak",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
-        "config": {"workload": names[args.config].replace("bf16", args.dtype, 1),
+        "config": {"workload": names[args.config].replace("bf16", args.dtype, 1)
+                   + ("_fused_keyranges" if fused else ""),
                    "segments": g.nseg,
                    "used_q_rows": int(np.sum(g.used_q)), "hq": g.hq, "hkv": g.hkv, "d": g.d,
                    "causal": bool(g.causal), "flop_per_step": flops,
                    "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-                   "algorithmic_hbm_bytes": algorithmic_bytes(g)},
+                   "algorithmic_hbm_bytes": algorithmic_bytes(
+                       g, keys=kr_lens if wl.key_ranges is not None else None)},
         "roofline": roofline,
     }
+    if merge_rec is not None:
+        res["merge"] = merge_rec
     if not args.no_cpu_baseline and args.config == 3 and args.dtype == "bf16":
         log("[bench] timing the oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_seconds)

@@ -33,8 +33,8 @@
  *     the diagonal when seqused_k < seqused_q) gets O = +0 and LSE = -inf;
  *   - LSE is the natural logarithm of sum_j exp(softmax_scale * q.k_j);
  *   - layouts (row-major, innermost last):
- *       Q   [total_q, hq,  d]      K [total_k, hkv, d]     V [total_k, hkv, d]
- *       O   [total_q, hq,  d]      LSE float [hq, total_q]
+ *       Q   [total_q, hq,  d]      K [total_k, hkv, d]     V [total_k, hkv, d_v]
+ *       O   [total_q, hq,  d_v]    LSE float [hq, total_q]
  *     Q, K, V and O share one element type (gvattn_dtype); LSE is fp32.
  *
  * Ownership and streams: every buffer is caller-owned device memory.  The
@@ -81,6 +81,9 @@ typedef enum gvattn_dtype {
 #define GVATTN_DEVERR_OFFSETS 4  /* cu_* decreasing, negative or past total_* */
 #define GVATTN_DEVERR_RANGE 8    /* a segment's rows span 2 GiB or more      */
 #define GVATTN_DEVERR_PLAN 16    /* gvattn_fwd_run found no matching plan   */
+#define GVATTN_DEVERR_KRANGES 32 /* key ranges: kr_off out of order or past
+                                    nranges, a range outside [0, total_k),
+                                    a negative length, 2^31 keys or more  */
 
 /* Largest partition count gvattn_lse_merge accepts. */
 #define GVATTN_MAX_PARTS 8
@@ -112,7 +115,10 @@ size_t gvattn_fwd_workspace_size(int32_t nseg, int32_t total_q, int32_t hq,
  *   nseg             >= 0 (0 is a no-op).
  *   total_q/total_k  rows of the Q/O and K/V buffers.
  *   hq, hkv          heads, hq % hkv == 0.
- *   d                head dim of Q, K and V: 64, 128 or 256.
+ *   d                head dim of Q and K: 64, 128 or 256.
+ *   d_v              head dim of V and O: 64, 128 or 256 (may differ from d;
+ *                    the pages' FA2 path requires equal dims and sends the
+ *                    rest to an FP32 fallback, PR #302 review).
  *   softmax_scale    finite and > 0 (typically 1/sqrt(d)).
  *   causal           0 or 1 (bottom-right within each segment).
  *   out, lse         device, written for used rows only; every other row is
@@ -125,7 +131,7 @@ int gvattn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                const int32_t* seqused_q, const int32_t* seqused_k,
                int32_t nseg, int32_t total_q, int32_t total_k,
-               int32_t hq, int32_t hkv, int32_t d,
+               int32_t hq, int32_t hkv, int32_t d, int32_t d_v,
                float softmax_scale, int32_t causal,
                void* out, float* lse,
                void* workspace, size_t workspace_bytes, void* hip_stream);
@@ -147,17 +153,50 @@ int gvattn_fwd_plan(int32_t dtype,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                     const int32_t* seqused_q, const int32_t* seqused_k,
                     int32_t nseg, int32_t total_q, int32_t total_k,
-                    int32_t hq, int32_t hkv, int32_t d, int32_t causal,
+                    int32_t hq, int32_t hkv, int32_t d, int32_t d_v, int32_t causal,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                    const int32_t* seqused_q, const int32_t* seqused_k,
                    int32_t nseg, int32_t total_q, int32_t total_k,
-                   int32_t hq, int32_t hkv, int32_t d,
+                   int32_t hq, int32_t hkv, int32_t d, int32_t d_v,
                    float softmax_scale, int32_t causal,
                    void* out, float* lse,
                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Forward over key ranges (TensorRT-LLM issue #18687, "Suggested fix", item
+ * 1: after the Ulysses all-to-all the key order is rank-major, so a sample's
+ * valid keys are several runs of rows, not one prefix).  Plan + attention
+ * in one call, as gvattn_fwd.
+ *
+ * Segment s's keys are the concatenation, in list order, of the K/V row
+ * ranges [kr_start[i], kr_start[i] + kr_len[i]) for i in [kr_off[s],
+ * kr_off[s + 1]).  Everything else is gvattn_fwd with seqused_k[s] = the
+ * total length of those ranges; the bottom-right causal alignment counts
+ * keys in the concatenated order.  A range may repeat or overlap another
+ * (each listed row is one key per listing).
+ *
+ *   kr_off         device int32 [nseg + 1], non-decreasing, within
+ *                  [0, nranges].
+ *   kr_start, kr_len  device int32 [nranges]; 0 <= kr_start, 0 <= kr_len,
+ *                  kr_start + kr_len <= total_k.  May be NULL when
+ *                  nranges == 0.
+ *   workspace      gvattn_fwd_workspace_size(...) bytes, as for gvattn_fwd.
+ *   other arguments as for gvattn_fwd (no cu_seqlens_k / seqused_k).
+ * A segment whose ranges break these rules is skipped (its rows are left
+ * untouched) and GVATTN_DEVERR_KRANGES is set in the workspace error word.
+ */
+int gvattn_fwd_ranges(int32_t dtype, const void* q, const void* k, const void* v,
+                      const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                      const int32_t* kr_off, const int32_t* kr_start,
+                      const int32_t* kr_len, int32_t nseg, int32_t nranges,
+                      int32_t total_q, int32_t total_k,
+                      int32_t hq, int32_t hkv, int32_t d, int32_t d_v,
+                      float softmax_scale, int32_t causal,
+                      void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * FP32 LSE merge of nparts partial results over key partitions (PR #312,

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     alloc_workspace,
     gvattn_fwd,
     gvattn_fwd_plan,
+    gvattn_fwd_ranges,
     gvattn_fwd_run,
     gvattn_fwd_workspace_size,
     gvattn_lse_merge,

@@ -30,6 +30,7 @@ GVATTN_DEVERR_USED_K = 2
 GVATTN_DEVERR_OFFSETS = 4
 GVATTN_DEVERR_RANGE = 8
 GVATTN_DEVERR_PLAN = 16
+GVATTN_DEVERR_KRANGES = 32
 
 GVATTN_MAX_PARTS = 8
 GVATTN_WORKSPACE_ALIGN = 256
@@ -40,14 +41,17 @@ _lib = None
 _i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 
 _FWD_ARGS = [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
-             _f32, _i32, _vp, _vp, _vp, _sz, _vp]
+             _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp]
 
 SIGNATURES = {
     "gvattn_fwd_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "gvattn_fwd": (ctypes.c_int, _FWD_ARGS),
     "gvattn_fwd_run": (ctypes.c_int, _FWD_ARGS),
     "gvattn_fwd_plan": (ctypes.c_int, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                       _i32, _i32, _vp, _sz, _vp]),
+                                       _i32, _i32, _i32, _vp, _sz, _vp]),
+    "gvattn_fwd_ranges": (ctypes.c_int, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                         _vp, _vp, _vp, _sz, _vp]),
     "gvattn_lse_merge": (ctypes.c_int, [_i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32,
                                         _i32, _vp, _vp, _vp, _vp]),
     "gvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -129,11 +133,14 @@ def _fwd_common(q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, 
     _need(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "q, k, v must be [rows, heads, dim]")
     total_q, hq, d = q.shape
     total_k, hkv, dk = k.shape
-    _need(tuple(v.shape) == (total_k, hkv, d), f"v must be {(total_k, hkv, d)}, got {tuple(v.shape)}")
+    dv = v.shape[2]
+    _need(tuple(v.shape[:2]) == (total_k, hkv),
+          f"v must be {(total_k, hkv, 'd_v')}, got {tuple(v.shape)}")
     _need(dk == d, f"q and k head dims differ ({d} vs {dk})")
     _need(q.dtype == k.dtype == v.dtype == out.dtype, "q, k, v and out must share one dtype")
     _need(hq % hkv == 0, f"hq={hq} must be a multiple of hkv={hkv}")
-    _need(tuple(out.shape) == (total_q, hq, d), f"out must be {(total_q, hq, d)}, got {tuple(out.shape)}")
+    _need(tuple(out.shape) == (total_q, hq, dv),
+          f"out must be {(total_q, hq, dv)}, got {tuple(out.shape)}")
     _need(lse.dtype == torch.float32 and tuple(lse.shape) == (hq, total_q),
           f"lse must be float32 [{hq}, {total_q}]")
     nseg = seqused_q.shape[0]
@@ -141,7 +148,7 @@ def _fwd_common(q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, 
     _check_i32_vec(cu_seqlens_k, nseg + 1, "cu_seqlens_k")
     _check_i32_vec(seqused_q, nseg, "seqused_q")
     _check_i32_vec(seqused_k, nseg, "seqused_k")
-    return nseg, total_q, total_k, hq, hkv, d
+    return nseg, total_q, total_k, hq, hkv, d, dv
 
 
 def gvattn_fwd_workspace_size(nseg: int, total_q: int, hq: int, hkv: int, d: int,
@@ -160,7 +167,7 @@ def alloc_workspace(nseg: int, total_q: int, hq: int, hkv: int, d: int, dtype: i
 
 def _fwd_call(fn_name, q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, lse,
               softmax_scale, causal, workspace, stream):
-    nseg, total_q, total_k, hq, hkv, d = _fwd_common(
+    nseg, total_q, total_k, hq, hkv, d, dv = _fwd_common(
         q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, lse)
     dt = _dtype_code(q)
     if workspace is None:
@@ -169,7 +176,7 @@ def _fwd_call(fn_name, q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k
     rc = getattr(lib, fn_name)(
         dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
         cu_seqlens_k.data_ptr(), seqused_q.data_ptr(), seqused_k.data_ptr(), nseg, total_q,
-        total_k, hq, hkv, d, float(softmax_scale), int(bool(causal)), out.data_ptr(),
+        total_k, hq, hkv, d, dv, float(softmax_scale), int(bool(causal)), out.data_ptr(),
         lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
     _check(rc, fn_name)
     return workspace
@@ -192,9 +199,36 @@ def gvattn_fwd_run(q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, ou
                      seqused_k, out, lse, softmax_scale, causal, workspace, stream)
 
 
+def gvattn_fwd_ranges(q, k, v, cu_seqlens_q, seqused_q, kr_off, kr_start, kr_len, out, lse,
+                      softmax_scale, causal=False, workspace=None, stream=None):
+    """Forward where segment s's keys are the K/V row ranges
+    [kr_start[i], kr_start[i] + kr_len[i]), i in [kr_off[s], kr_off[s+1]),
+    concatenated in order.  Returns the workspace."""
+    nseg = seqused_q.shape[0]
+    # reuse the shape checks of the prefix form with stand-in key vectors
+    _, total_q, total_k, hq, hkv, d, dv = _fwd_common(
+        q, k, v, cu_seqlens_q, cu_seqlens_q, seqused_q, seqused_q, out, lse)
+    _check_i32_vec(kr_off, nseg + 1, "kr_off")
+    nranges = kr_start.shape[0] if kr_start.dim() == 1 else -1
+    _check_i32_vec(kr_start, nranges, "kr_start")
+    _check_i32_vec(kr_len, nranges, "kr_len")
+    dt = _dtype_code(q)
+    if workspace is None:
+        workspace = alloc_workspace(nseg, total_q, hq, hkv, d, dt, q.device)
+    rc = load_library().gvattn_fwd_ranges(
+        dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+        seqused_q.data_ptr(), kr_off.data_ptr(),
+        kr_start.data_ptr() if nranges > 0 else None,
+        kr_len.data_ptr() if nranges > 0 else None, nseg, nranges, total_q, total_k, hq, hkv,
+        d, dv, float(softmax_scale), int(bool(causal)), out.data_ptr(), lse.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
+    _check(rc, "gvattn_fwd_ranges")
+    return workspace
+
+
 def gvattn_fwd_plan(dtype: int, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, total_q: int,
                     total_k: int, hq: int, hkv: int, d: int, causal: bool, workspace=None,
-                    stream=None):
+                    stream=None, d_v: int | None = None):
     """Build the tile plan of a geometry into `workspace` (allocated when
     None) and return the workspace."""
     nseg = seqused_q.shape[0]
@@ -206,7 +240,8 @@ def gvattn_fwd_plan(dtype: int, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k
         workspace = alloc_workspace(nseg, total_q, hq, hkv, d, dtype, seqused_q.device)
     rc = load_library().gvattn_fwd_plan(
         dtype, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), seqused_q.data_ptr(),
-        seqused_k.data_ptr(), nseg, total_q, total_k, hq, hkv, d, int(bool(causal)),
+        seqused_k.data_ptr(), nseg, total_q, total_k, hq, hkv, d, d if d_v is None else d_v,
+        int(bool(causal)),
         workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
     _check(rc, "gvattn_fwd_plan")
     return workspace

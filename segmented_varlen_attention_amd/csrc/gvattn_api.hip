@@ -70,14 +70,15 @@ bool dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
 int esize(int32_t dtype) { return dtype == GVATTN_FP32 ? 4 : 2; }
 
 int check_sizes(int32_t dtype, int32_t nseg, int32_t total_q, int32_t total_k, int32_t hq,
-                int32_t hkv, int32_t d, int32_t causal) {
+                int32_t hkv, int32_t d, int32_t dv, int32_t causal) {
   if (!dtype_ok(dtype)) return GVATTN_ERR_UNSUPPORTED;
   if (nseg < 0 || total_q < 0 || total_k < 0 || hq <= 0 || hkv <= 0) return GVATTN_ERR_INVALID_ARG;
   if (hq % hkv != 0) return GVATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return GVATTN_ERR_INVALID_ARG;
-  if (!dim_ok(d)) return GVATTN_ERR_UNSUPPORTED;
+  if (!dim_ok(d) || !dim_ok(dv)) return GVATTN_ERR_UNSUPPORTED;
   // one packed row (all heads) must stay well inside a 32-bit byte offset
-  if ((int64_t)hq * d * esize(dtype) > (int64_t(1) << 24)) return GVATTN_ERR_UNSUPPORTED;
+  if ((int64_t)hq * (d > dv ? d : dv) * esize(dtype) > (int64_t(1) << 24))
+    return GVATTN_ERR_UNSUPPORTED;
   return GVATTN_OK;
 }
 
@@ -90,7 +91,7 @@ int check_workspace(const void* ws, size_t bytes, int32_t nseg, int32_t total_q,
 
 Geometry make_geom(const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
                    const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
-                   int32_t hq, int32_t hkv, int32_t d, int32_t causal) {
+                   int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t causal) {
   Geometry g;
   g.cu_q = cu_q;
   g.cu_k = cu_k;
@@ -102,7 +103,12 @@ Geometry make_geom(const int32_t* cu_q, const int32_t* cu_k, const int32_t* used
   g.hq = hq;
   g.hkv = hkv;
   g.d = d;
+  g.dv = dv;
   g.causal = causal;
+  g.kr_off = nullptr;
+  g.kr_start = nullptr;
+  g.kr_len = nullptr;
+  g.nranges = 0;
   return g;
 }
 
@@ -113,9 +119,10 @@ int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
   a.ws = view_workspace(ws, g.nseg, g.total_q, t.rows);
   a.rows = t.rows;
   a.max_tiles = (int32_t)max_tiles(g.nseg, g.total_q, t.rows);
-  a.key = plan_key(t.rows, g.causal, g.nseg);
-  a.q_row_bytes = (int64_t)g.hq * g.d * esize(dtype);
-  a.k_row_bytes = (int64_t)g.hkv * g.d * esize(dtype);
+  a.key = plan_key(t.rows, g.causal, g.nseg, (g.kr_off != nullptr) | (g.d << 1) | (g.dv << 10));
+  const int dmax = g.d > g.dv ? g.d : g.dv;
+  a.q_row_bytes = (int64_t)g.hq * dmax * esize(dtype);
+  a.k_row_bytes = (int64_t)g.hkv * dmax * esize(dtype);
   return launch_plan(a, stream) == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
 }
 
@@ -131,7 +138,7 @@ int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   a.out = out;
   a.lse = lse;
   a.scale_log2 = scale * kLog2e;
-  a.key = plan_key(t.rows, g.causal, g.nseg);
+  a.key = plan_key(t.rows, g.causal, g.nseg, (g.kr_off != nullptr) | (g.d << 1) | (g.dv << 10));
   a.n_head_chunks = g.hq / t.gf;
   const int64_t max_work = max_tiles(g.nseg, g.total_q, t.rows) * a.n_head_chunks;
   bool ok = false;
@@ -144,9 +151,9 @@ int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const
 int check_fwd_args(int32_t dtype, const void* q, const void* k, const void* v,
                    const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
                    const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
-                   int32_t hq, int32_t hkv, int32_t d, float scale, int32_t causal,
-                   void* out, float* lse, void* ws, size_t ws_bytes) {
-  int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, causal);
+                   int32_t hq, int32_t hkv, int32_t d, int32_t dv, float scale,
+                   int32_t causal, void* out, float* lse, void* ws, size_t ws_bytes) {
+  int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, dv, causal);
   if (rc != GVATTN_OK) return rc;
   if (!(scale > 0.f) || !isfinite(scale)) return GVATTN_ERR_INVALID_ARG;
   if (nseg == 0) return GVATTN_OK;
@@ -165,7 +172,7 @@ extern "C" {
 
 size_t gvattn_fwd_workspace_size(int32_t nseg, int32_t total_q, int32_t hq, int32_t hkv,
                                  int32_t d, int32_t dtype) {
-  if (check_sizes(dtype, nseg, total_q, 0, hq, hkv, d, 0) != GVATTN_OK) return 0;
+  if (check_sizes(dtype, nseg, total_q, 0, hq, hkv, d, d, 0) != GVATTN_OK) return 0;
   const TileShape t = choose_shape(dtype, hq, hkv, d);
   return workspace_bytes(nseg, total_q, t.rows);
 }
@@ -173,30 +180,33 @@ size_t gvattn_fwd_workspace_size(int32_t nseg, int32_t total_q, int32_t hq, int3
 int gvattn_fwd_plan(int32_t dtype, const int32_t* cu_q, const int32_t* cu_k,
                     const int32_t* used_q, const int32_t* used_k, int32_t nseg,
                     int32_t total_q, int32_t total_k, int32_t hq, int32_t hkv, int32_t d,
-                    int32_t causal, void* workspace, size_t workspace_bytes_,
+                    int32_t d_v, int32_t causal, void* workspace, size_t workspace_bytes_,
                     void* hip_stream) {
-  int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, causal);
+  int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
   if (rc != GVATTN_OK) return rc;
   if (nseg == 0) return GVATTN_OK;
   if (!cu_q || !cu_k || !used_q || !used_k) return GVATTN_ERR_INVALID_ARG;
   const TileShape t = choose_shape(dtype, hq, hkv, d);
   rc = check_workspace(workspace, workspace_bytes_, nseg, total_q, t.rows);
   if (rc != GVATTN_OK) return rc;
-  const Geometry g = make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, causal);
+  const Geometry g =
+      make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
   return do_plan(dtype, g, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
 int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
                    const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
                    const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
-                   int32_t hq, int32_t hkv, int32_t d, float softmax_scale, int32_t causal,
+                   int32_t hq, int32_t hkv, int32_t d, int32_t d_v, float softmax_scale,
+                   int32_t causal,
                    void* out, float* lse, void* workspace, size_t workspace_bytes_,
                    void* hip_stream) {
   int rc = check_fwd_args(dtype, q, k, v, cu_q, cu_k, used_q, used_k, nseg, total_q, total_k,
-                          hq, hkv, d, softmax_scale, causal, out, lse, workspace,
+                          hq, hkv, d, d_v, softmax_scale, causal, out, lse, workspace,
                           workspace_bytes_);
   if (rc != GVATTN_OK || nseg == 0) return rc;
-  const Geometry g = make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, causal);
+  const Geometry g =
+      make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
   return do_run(dtype, g, q, k, v, softmax_scale, out, lse, workspace,
                 static_cast<hipStream_t>(hip_stream));
 }
@@ -204,14 +214,45 @@ int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
 int gvattn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
                const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
-               int32_t hq, int32_t hkv, int32_t d, float softmax_scale, int32_t causal,
+               int32_t hq, int32_t hkv, int32_t d, int32_t d_v, float softmax_scale,
+               int32_t causal,
                void* out, float* lse, void* workspace, size_t workspace_bytes_,
                void* hip_stream) {
   int rc = check_fwd_args(dtype, q, k, v, cu_q, cu_k, used_q, used_k, nseg, total_q, total_k,
-                          hq, hkv, d, softmax_scale, causal, out, lse, workspace,
+                          hq, hkv, d, d_v, softmax_scale, causal, out, lse, workspace,
                           workspace_bytes_);
   if (rc != GVATTN_OK || nseg == 0) return rc;
-  const Geometry g = make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, causal);
+  const Geometry g =
+      make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  rc = do_plan(dtype, g, workspace, s);
+  if (rc != GVATTN_OK) return rc;
+  return do_run(dtype, g, q, k, v, softmax_scale, out, lse, workspace, s);
+}
+
+int gvattn_fwd_ranges(int32_t dtype, const void* q, const void* k, const void* v,
+                      const int32_t* cu_q, const int32_t* used_q, const int32_t* kr_off,
+                      const int32_t* kr_start, const int32_t* kr_len, int32_t nseg,
+                      int32_t nranges, int32_t total_q, int32_t total_k, int32_t hq,
+                      int32_t hkv, int32_t d, int32_t d_v, float softmax_scale,
+                      int32_t causal, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes_, void* hip_stream) {
+  int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
+  if (rc != GVATTN_OK) return rc;
+  if (nranges < 0) return GVATTN_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return GVATTN_ERR_INVALID_ARG;
+  if (nseg == 0) return GVATTN_OK;
+  if (!q || !k || !v || !cu_q || !used_q || !kr_off || !out || !lse) return GVATTN_ERR_INVALID_ARG;
+  if (nranges > 0 && (!kr_start || !kr_len)) return GVATTN_ERR_INVALID_ARG;
+  const TileShape t = choose_shape(dtype, hq, hkv, d);
+  rc = check_workspace(workspace, workspace_bytes_, nseg, total_q, t.rows);
+  if (rc != GVATTN_OK) return rc;
+  Geometry g = make_geom(cu_q, nullptr, used_q, nullptr, nseg, total_q, total_k, hq, hkv, d,
+                         d_v, causal);
+  g.kr_off = kr_off;
+  g.kr_start = kr_start;
+  g.kr_len = kr_len;
+  g.nranges = nranges;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   rc = do_plan(dtype, g, workspace, s);
   if (rc != GVATTN_OK) return rc;

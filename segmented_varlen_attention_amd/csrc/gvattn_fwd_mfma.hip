@@ -65,23 +65,28 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int D, int GF, int RB, int NKB>
+// DQ: head dim of Q and K; DV: head dim of V and O.
+template <int DQ, int DV, int GF, int RB, int NKB>
 struct Cfg {
   static constexpr int NW = GF * RB;          // waves per workgroup
   static constexpr int NT = 64 * NW;          // threads
   static constexpr int NKB_ = NKB;            // 32-key blocks per tile (1 or 2)
   static constexpr int BN = 32 * NKB;         // keys per tile
-  static constexpr int CH = D / 8;            // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;        // K + V
-  static constexpr int DMA_PER_TILE = TILE_BYTES / 1024;    // 1 KB per wave instruction
-  static constexpr int OP = D + 8;            // O staging row pitch (elements)
+  static constexpr int CHK = DQ / 8;          // 16-byte chunks per K row
+  static constexpr int CHV = DV / 8;          // 16-byte chunks per V / O row
+  static constexpr int K_TILE_BYTES = BN * DQ * 2;
+  static constexpr int V_TILE_BYTES = BN * DV * 2;
+  static constexpr int STAGE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
+  static constexpr int DMA_K = K_TILE_BYTES / 1024;  // 1 KB per wave instruction
+  static constexpr int DMA_V = V_TILE_BYTES / 1024;
+  static constexpr int OP = DV + 8;           // O staging row pitch (elements)
   static constexpr int O_BYTES = NW * 32 * OP * 2;
   static constexpr int LDS_BYTES = (2 * STAGE_BYTES > O_BYTES) ? 2 * STAGE_BYTES : O_BYTES;
-  static constexpr int KK = D / 16;           // k-steps of the score MFMA
-  static constexpr int DB = D / 32;           // 32-wide d blocks of O
-  static constexpr int MIN_BLOCKS = (D <= 128) ? (NKB == 1 ? 3 : 2) : 1;
-  static constexpr int NDMA = (DMA_PER_TILE + NW - 1) / NW;  // DMA instructions per wave
+  static constexpr int KK = DQ / 16;          // k-steps of the score MFMA
+  static constexpr int DB = DV / 32;          // 32-wide d blocks of O
+  static constexpr int MIN_BLOCKS = (DQ <= 128 && DV <= 128) ? (NKB == 1 ? 3 : 2) : 1;
+  static constexpr int NDMA_K = (DMA_K + NW - 1) / NW;  // DMA instructions per wave
+  static constexpr int NDMA_V = (DMA_V + NW - 1) / NW;
 };
 
 // XOR swizzles of the 16-byte chunk index inside a row, chosen so that the
@@ -136,10 +141,18 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <typename T, int D, int GF, int RB, int NKB>
-__global__ __launch_bounds__((Cfg<D, GF, RB, NKB>::NT), (Cfg<D, GF, RB, NKB>::MIN_BLOCKS))
+// Position of a key-range cursor: range i (rows row0 .. row0 + len - 1 of
+// K/V, keys pos .. pos + len - 1 of the segment's concatenated sequence),
+// local tile lt of its nt tiles.  nt == 0: no tiles left.
+struct KeyCursor {
+  int i, row0, len, pos, lt, nt;
+};
+
+template <typename T, int DQ, int DV, int GF, int RB, int NKB, bool KR>
+__global__ __launch_bounds__((Cfg<DQ, DV, GF, RB, NKB>::NT),
+                             (Cfg<DQ, DV, GF, RB, NKB>::MIN_BLOCKS))
 void fwd_mfma_kernel(FwdArgs a) {
-  using C = Cfg<D, GF, RB, NKB>;
+  using C = Cfg<DQ, DV, GF, RB, NKB>;
   using E = Elem<T>;
   using v8 = typename E::v8;
   using v4 = typename E::v4;
@@ -160,21 +173,28 @@ void fwd_mfma_kernel(FwdArgs a) {
   const int r32 = lane & 31, hh = lane >> 5;
   const int hf = wave % GF, rb = wave / GF;
   const int G = a.g.hq / a.g.hkv;
-  const uint32_t qstride = (uint32_t)a.g.hq * D * 2;    // bytes between rows
-  const uint32_t kstride = (uint32_t)a.g.hkv * D * 2;
+  // bytes between consecutive rows of Q, K, V and O
+  const uint32_t qstride = (uint32_t)a.g.hq * DQ * 2;
+  const uint32_t kstride = (uint32_t)a.g.hkv * DQ * 2;
+  const uint32_t vstride = (uint32_t)a.g.hkv * DV * 2;
+  const uint32_t ostride = (uint32_t)a.g.hq * DV * 2;
   const float c = a.scale_log2;
 
   // Per-lane global offsets of this wave's K/V DMA instructions: slot s of
   // a tile (1 KB per instruction, 16 B per lane) holds row s / CH, chunk
   // (s % CH) ^ swizzle(row).
-  uint32_t koff[C::NDMA], voff[C::NDMA];
+  uint32_t koff[C::NDMA_K], voff[C::NDMA_V];
 #pragma unroll
-  for (int i = 0; i < C::NDMA; ++i) {
-    const int inst = wave + i * C::NW;
-    const int s = inst * 64 + lane;
-    const int row = s / C::CH, pc = s % C::CH;
-    koff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_k<D>(row)) * 16);
-    voff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_v<D>(row)) * 16);
+  for (int i = 0; i < C::NDMA_K; ++i) {
+    const int s = (wave + i * C::NW) * 64 + lane;
+    const int row = s / C::CHK, pc = s % C::CHK;
+    koff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_k<DQ>(row)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < C::NDMA_V; ++i) {
+    const int s = (wave + i * C::NW) * 64 + lane;
+    const int row = s / C::CHV, pc = s % C::CHV;
+    voff[i] = (uint32_t)row * vstride + (uint32_t)((pc ^ swz_v<DV>(row)) * 16);
   }
 
   // ds_read_b64_tr_b16 addressing inside each 16-lane group: local lane
@@ -222,33 +242,82 @@ void fwd_mfma_kernel(FwdArgs a) {
     const int head = head0 + hf;
     const int kvh = head0 / G;
     const int q0 = __builtin_amdgcn_readfirstlane(a.g.cu_q[seg]);
-    const int k0 = __builtin_amdgcn_readfirstlane(a.g.cu_k[seg]);
     const int uq = __builtin_amdgcn_readfirstlane(a.g.used_q[seg]);
-    const int uk = __builtin_amdgcn_readfirstlane(a.g.used_k[seg]);
+    // keys: the used prefix at k0, or (KR) the concatenation of the
+    // segment's ranges, whose total length the plan stored
+    const int k0 = KR ? 0 : __builtin_amdgcn_readfirstlane(a.g.cu_k[seg]);
+    const int uk = __builtin_amdgcn_readfirstlane(KR ? a.ws.seg_keys[seg] : a.g.used_k[seg]);
     const int wr0 = row0 + rb * 32;                  // first row of this wave
     const int r_last = min(row0 + 32 * RB, uq) - 1;  // last used row of the tile
     int kend = uk;
     if (a.g.causal) kend = max(0, min(uk, r_last + uk - uq + 1));
-    const int n_kt = (kend + C::BN - 1) / C::BN;
 
-    const T* qbase = static_cast<const T*>(a.q) + ((int64_t)q0 * a.g.hq + head) * D;
-    const uint32_t qbytes = uq > 0 ? (uint32_t)(uq - 1) * qstride + D * 2 : 0u;
+    // Key-range form: tiles never straddle two ranges; cursor `cur` is the
+    // tile being computed, `nx` the one being loaded.
+    const int kr_end = KR ? __builtin_amdgcn_readfirstlane(a.g.kr_off[seg + 1]) : 0;
+    auto settle = [&](KeyCursor& c) {  // first range from c.i on with a tile below kend
+      c.nt = 0;
+      while (c.i < kr_end && c.pos < kend) {
+        c.row0 = __builtin_amdgcn_readfirstlane(a.g.kr_start[c.i]);
+        c.len = __builtin_amdgcn_readfirstlane(a.g.kr_len[c.i]);
+        const int n = min(c.len, kend - c.pos);
+        c.lt = 0;
+        c.nt = n > 0 ? (n + C::BN - 1) / C::BN : 0;
+        if (c.nt > 0) return;
+        c.pos += c.len;
+        ++c.i;
+      }
+      c.nt = 0;
+    };
+    auto advance = [&](KeyCursor& c) {
+      if (c.lt + 1 < c.nt) {
+        ++c.lt;
+      } else {
+        c.pos += c.len;
+        ++c.i;
+        settle(c);
+      }
+    };
+    KeyCursor cur{0, 0, 0, 0, 0, 0};
+    int n_kt;
+    if constexpr (KR) {
+      cur.i = __builtin_amdgcn_readfirstlane(a.g.kr_off[seg]);
+      settle(cur);
+      n_kt = 0;
+      for (KeyCursor c = cur; c.nt > 0; c.pos += c.len, ++c.i, settle(c)) n_kt += c.nt;
+    } else {
+      n_kt = (kend + C::BN - 1) / C::BN;
+    }
+
+    const T* qbase = static_cast<const T*>(a.q) + ((int64_t)q0 * a.g.hq + head) * DQ;
+    const uint32_t qbytes = uq > 0 ? (uint32_t)(uq - 1) * qstride + DQ * 2 : 0u;
     const auto qr = make_rsrc(qbase, qbytes);
-    const int64_t kvoff = ((int64_t)k0 * a.g.hkv + kvh) * D;
-    const uint32_t kbytes = uk > 0 ? (uint32_t)(uk - 1) * kstride + D * 2 : 0u;
-    const auto kr = make_rsrc(static_cast<const T*>(a.k) + kvoff, kbytes);
-    const auto vr = make_rsrc(static_cast<const T*>(a.v) + kvoff, kbytes);
+    // K and V rows [first, first + n) of this KV head as bounded resources
+    auto k_rsrc = [&](int first, int n) {
+      return make_rsrc(static_cast<const T*>(a.k) + ((int64_t)first * a.g.hkv + kvh) * DQ,
+                       n > 0 ? (uint32_t)(n - 1) * kstride + DQ * 2 : 0u);
+    };
+    auto v_rsrc = [&](int first, int n) {
+      return make_rsrc(static_cast<const T*>(a.v) + ((int64_t)first * a.g.hkv + kvh) * DV,
+                       n > 0 ? (uint32_t)(n - 1) * vstride + DV * 2 : 0u);
+    };
+    const int kfirst = KR ? cur.row0 : k0, klen = KR ? cur.len : uk;
+    const auto kr = k_rsrc(kfirst, klen);
+    const auto vr = v_rsrc(kfirst, klen);
 
     auto issue_tile = [&](int kt) {
       char* st = lds + (kt & 1) * C::STAGE_BYTES;
-      const uint32_t soff = (uint32_t)kt * C::BN * kstride;
+      const uint32_t soffk = (uint32_t)kt * C::BN * kstride;
+      const uint32_t soffv = (uint32_t)kt * C::BN * vstride;
 #pragma unroll
-      for (int i = 0; i < C::NDMA; ++i) {
+      for (int i = 0; i < C::NDMA_K; ++i) {
         const int inst = wave + i * C::NW;
-        if (inst < C::DMA_PER_TILE) {
-          dma16(kr, st + inst * 1024, koff[i], soff);
-          dma16(vr, st + C::TILE_BYTES + inst * 1024, voff[i], soff);
-        }
+        if (inst < C::DMA_K) dma16(kr, st + inst * 1024, koff[i], soffk);
+      }
+#pragma unroll
+      for (int i = 0; i < C::NDMA_V; ++i) {
+        const int inst = wave + i * C::NW;
+        if (inst < C::DMA_V) dma16(vr, st + C::K_TILE_BYTES + inst * 1024, voff[i], soffv);
       }
     };
 
@@ -272,27 +341,35 @@ void fwd_mfma_kernel(FwdArgs a) {
     const int lim = a.g.causal ? min(uk, row + uk - uq + 1) : uk;
     const int lim_w = a.g.causal ? min(uk, wr0 + uk - uq + 1) : uk;  // wave minimum
 
+    KeyCursor nx = cur;
     for (int kt = 0; kt < n_kt; ++kt) {
       wait_vmem();
       __syncthreads();
       const char* Ks = lds + (kt & 1) * C::STAGE_BYTES;
-      const char* Vs = Ks + C::TILE_BYTES;
+      const char* Vs = Ks + C::K_TILE_BYTES;
+      if constexpr (KR) advance(nx);
 
       // The loads of tile kt + 1 are spread between the score MFMAs, so
       // their issue overlaps matrix-core work.  Without a next tile they go
       // through zero-size buffer resources (every load returns zero into the
       // stage nobody reads any more), which keeps the phase branch-free.
-      const uint32_t nbytes = (kt + 1 < n_kt) ? kbytes : 0u;
-      const auto krn = make_rsrc(static_cast<const T*>(a.k) + kvoff, nbytes);
-      const auto vrn = make_rsrc(static_cast<const T*>(a.v) + kvoff, nbytes);
+      const int nlen = (kt + 1 < n_kt) ? (KR ? nx.len : uk) : 0;
+      const int nfirst = KR ? nx.row0 : k0;
+      const auto krn = k_rsrc(nfirst, nlen);
+      const auto vrn = v_rsrc(nfirst, nlen);
       char* stn = lds + ((kt + 1) & 1) * C::STAGE_BYTES;
-      const uint32_t soffn = (uint32_t)(kt + 1) * C::BN * kstride;
+      const uint32_t ntile = (uint32_t)(KR ? nx.lt : kt + 1) * C::BN;
+      const uint32_t soffkn = ntile * kstride, soffvn = ntile * vstride;
+      // j < NDMA_K: K instruction j of this wave, then the V instructions
       auto issue_one = [&](int j) {
-        const int i = j % C::NDMA, which = j / C::NDMA;
-        const int inst = wave + i * C::NW;
-        if (i + 1 < C::NDMA || inst < C::DMA_PER_TILE) {
-          if (which == 0) dma16(krn, stn + inst * 1024, koff[i], soffn);
-          else dma16(vrn, stn + C::TILE_BYTES + inst * 1024, voff[i], soffn);
+        if (j < C::NDMA_K) {
+          const int inst = wave + j * C::NW;
+          if (j + 1 < C::NDMA_K || inst < C::DMA_K) dma16(krn, stn + inst * 1024, koff[j], soffkn);
+        } else {
+          const int i = j - C::NDMA_K;
+          const int inst = wave + i * C::NW;
+          if (i + 1 < C::NDMA_V || inst < C::DMA_V)
+            dma16(vrn, stn + C::K_TILE_BYTES + inst * 1024, voff[i], soffvn);
         }
       };
 
@@ -302,25 +379,29 @@ void fwd_mfma_kernel(FwdArgs a) {
       for (int kb = 0; kb < C::NKB_; ++kb) {
         s[kb] = f32x16{};
         const int krow = kb * 32 + r32;
-        const char* kp = Ks + krow * (D * 2);
-        const int sw = swz_k<D>(krow);
+        const char* kp = Ks + krow * (DQ * 2);
+        const int sw = swz_k<DQ>(krow);
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk) {
           const v8 ka = *reinterpret_cast<const v8*>(kp + (((2 * kk + hh) ^ sw) << 4));
           s[kb] = E::mfma(ka, qf[kk], s[kb]);
           const int step = kb * C::KK + kk;
+          constexpr int NJ = C::NDMA_K + C::NDMA_V;
 #pragma unroll
-          for (int j = 0; j < 2 * C::NDMA; ++j)
-            if ((j * C::NKB_ * C::KK) / (2 * C::NDMA) == step) issue_one(j);
+          for (int j = 0; j < NJ; ++j)
+            if ((j * C::NKB_ * C::KK) / NJ == step) issue_one(j);
         }
       }
 
-      // key-padding / causal mask on boundary tiles
-      const int kbase = kt * C::BN;
-      if (kbase + C::BN > lim_w) {
+      // key-padding / causal mask on boundary tiles (in the key-range form
+      // keys past the end of the tile's range are masked as well)
+      const int kbase = KR ? cur.pos + cur.lt * C::BN : kt * C::BN;
+      const int lim_t = KR ? min(lim, cur.pos + cur.len) : lim;
+      const int lim_wt = KR ? min(lim_w, cur.pos + cur.len) : lim_w;
+      if (kbase + C::BN > lim_wt) {
         // score (kb, v) is key kbase + kb*32 + 8*(v/4) + 4*hh + v%4: it is
-        // masked when its compile-time offset reaches lim - kbase - 4*hh
-        int nv = lim - kbase - 4 * hh;
+        // masked when its compile-time offset reaches lim_t - kbase - 4*hh
+        int nv = lim_t - kbase - 4 * hh;
         asm volatile("" : "+v"(nv));  // defined here: the compares stay in the branch
 #pragma unroll
         for (int kb = 0; kb < C::NKB_; ++kb)
@@ -378,13 +459,14 @@ void fwd_mfma_kernel(FwdArgs a) {
           for (int a2 = 0; a2 < 2; ++a2) {
             const int r_lo = kb * 32 + a2 * 16 + vrow_l;
             const int r_hi = r_lo + 8;
-            const i16x4 lo = read_tr(Vs + r_lo * (D * 2) + ((ch ^ swz_v<D>(r_lo)) << 4) + within);
-            const i16x4 hi = read_tr(Vs + r_hi * (D * 2) + ((ch ^ swz_v<D>(r_hi)) << 4) + within);
+            const i16x4 lo = read_tr(Vs + r_lo * (DV * 2) + ((ch ^ swz_v<DV>(r_lo)) << 4) + within);
+            const i16x4 hi = read_tr(Vs + r_hi * (DV * 2) + ((ch ^ swz_v<DV>(r_hi)) << 4) + within);
             const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             const v8 va = __builtin_bit_cast(v8, both);
             o[db] = E::mfma(va, pb[kb][a2], o[db]);
           }
       }
+      if constexpr (KR) cur = nx;
     }
 
     // epilogue: normalise, LSE, stage O through LDS, full-row stores
@@ -408,25 +490,26 @@ void fwd_mfma_kernel(FwdArgs a) {
       }
     __syncthreads();
     {
-      T* obase = static_cast<T*>(a.out) + ((int64_t)q0 * a.g.hq + head) * D;
-      const auto orr = make_rsrc(obase, qbytes);
+      T* obase = static_cast<T*>(a.out) + ((int64_t)q0 * a.g.hq + head) * DV;
+      const auto orr = make_rsrc(obase, uq > 0 ? (uint32_t)(uq - 1) * ostride + DV * 2 : 0u);
 #pragma unroll
-      for (int it = 0; it < D / 16; ++it) {
+      for (int it = 0; it < DV / 16; ++it) {
         const int idx = it * 64 + lane;
-        const int r = idx / C::CH, ch = idx % C::CH;
+        const int r = idx / C::CHV, ch = idx % C::CHV;
         const u32x4 val = *reinterpret_cast<const u32x4*>(Os + r * C::OP + 8 * ch);
-        buf_store16(orr, (uint32_t)(wr0 + r) * qstride + ch * 16, val);
+        buf_store16(orr, (uint32_t)(wr0 + r) * ostride + ch * 16, val);
       }
     }
     __syncthreads();  // staging area is reused by the next item's K/V loads
   }
 }
 
-template <typename T, int D, int GF, int RB>
+template <typename T, int DQ, int DV, int GF, int RB>
 hipError_t launch_one(const FwdArgs& a, int64_t max_work, hipStream_t s) {
-  constexpr int NKB = (D <= 128) ? 1 : 2;
-  using C = Cfg<D, GF, RB, NKB>;
-  auto kern = fwd_mfma_kernel<T, D, GF, RB, NKB>;
+  constexpr int NKB = (DQ <= 128 && DV <= 128) ? 1 : 2;
+  using C = Cfg<DQ, DV, GF, RB, NKB>;
+  auto kern = (a.g.kr_off != nullptr) ? fwd_mfma_kernel<T, DQ, DV, GF, RB, NKB, true>
+                                      : fwd_mfma_kernel<T, DQ, DV, GF, RB, NKB, false>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), C::NT, max_work);
   if (grid <= 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
   FwdArgs args = a;
@@ -436,16 +519,27 @@ hipError_t launch_one(const FwdArgs& a, int64_t max_work, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int DQ, int DV>
 hipError_t launch_d(const FwdArgs& a, const TileShape& t, int64_t max_work, hipStream_t s,
                     bool* ok) {
   *ok = true;
   switch (t.gf) {
-    case 4: return launch_one<T, D, 4, 1>(a, max_work, s);
-    case 3: return launch_one<T, D, 3, 1>(a, max_work, s);
-    case 2: return launch_one<T, D, 2, 2>(a, max_work, s);
-    case 1: return launch_one<T, D, 1, 4>(a, max_work, s);
+    case 4: return launch_one<T, DQ, DV, 4, 1>(a, max_work, s);
+    case 3: return launch_one<T, DQ, DV, 3, 1>(a, max_work, s);
+    case 2: return launch_one<T, DQ, DV, 2, 2>(a, max_work, s);
+    case 1: return launch_one<T, DQ, DV, 1, 4>(a, max_work, s);
     default: *ok = false; return hipSuccess;
+  }
+}
+
+template <typename T, int DQ>
+hipError_t launch_dq(const FwdArgs& a, const TileShape& t, int64_t max_work, hipStream_t s,
+                     bool* supported) {
+  switch (a.g.dv) {
+    case 64: return launch_d<T, DQ, 64>(a, t, max_work, s, supported);
+    case 128: return launch_d<T, DQ, 128>(a, t, max_work, s, supported);
+    case 256: return launch_d<T, DQ, 256>(a, t, max_work, s, supported);
+    default: *supported = false; return hipSuccess;
   }
 }
 
@@ -453,9 +547,9 @@ template <typename T>
 hipError_t launch_t(const FwdArgs& a, const TileShape& t, int64_t max_work, hipStream_t s,
                     bool* supported) {
   switch (a.g.d) {
-    case 64: return launch_d<T, 64>(a, t, max_work, s, supported);
-    case 128: return launch_d<T, 128>(a, t, max_work, s, supported);
-    case 256: return launch_d<T, 256>(a, t, max_work, s, supported);
+    case 64: return launch_dq<T, 64>(a, t, max_work, s, supported);
+    case 128: return launch_dq<T, 128>(a, t, max_work, s, supported);
+    case 256: return launch_dq<T, 256>(a, t, max_work, s, supported);
     default: *supported = false; return hipSuccess;
   }
 }

@@ -12,6 +12,7 @@ namespace gvattn {
 // ---------------------------------------------------------------------------
 // Workspace: [PlanHeader (256 B)] [tile list: int2 x max_tiles]
 //            [per-segment tile offsets: int32 x (nseg + 1)]
+//            [per-segment key count: int32 x (nseg + 1)] (key-range form)
 // A tile is (segment, first row in the segment); the list is sorted by
 // decreasing number of key tiles so that the persistent kernel takes the
 // longest work first.
@@ -58,12 +59,13 @@ inline TileShape choose_shape(int dtype, int hq, int hkv, int d) {
   return t;
 }
 
-inline uint32_t plan_key(int rows, int causal, int nseg) {
+inline uint32_t plan_key(int rows, int causal, int nseg, int ranges) {
   uint32_t h = 2166136261u;
   auto mix = [&h](uint32_t x) { h = (h ^ x) * 16777619u; };
   mix((uint32_t)rows);
   mix((uint32_t)causal);
   mix((uint32_t)nseg);
+  mix((uint32_t)ranges);
   return h | 1u;  // never 0, so a zeroed workspace never matches
 }
 
@@ -76,7 +78,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline size_t workspace_bytes(int64_t nseg, int64_t total_q, int rows) {
   size_t b = sizeof(PlanHeader);
   b += align_up((size_t)max_tiles(nseg, total_q, rows) * 8, 256);
-  b += align_up((size_t)(nseg + 1) * 4, 256);
+  b += 2 * align_up((size_t)(nseg + 1) * 4, 256);
   return b;
 }
 
@@ -84,6 +86,7 @@ struct WorkspaceView {
   PlanHeader* header;
   int2* tiles;
   int32_t* seg_tile_off;
+  int32_t* seg_keys;  // key-range form: total key count of each segment
 };
 
 inline WorkspaceView view_workspace(void* ws, int64_t nseg, int64_t total_q, int rows) {
@@ -94,21 +97,31 @@ inline WorkspaceView view_workspace(void* ws, int64_t nseg, int64_t total_q, int
   v.tiles = reinterpret_cast<int2*>(p);
   p += align_up((size_t)max_tiles(nseg, total_q, rows) * 8, 256);
   v.seg_tile_off = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)(nseg + 1) * 4, 256);
+  v.seg_keys = reinterpret_cast<int32_t*>(p);
   return v;
 }
 
-// Geometry shared by plan and forward kernels.
+// Geometry shared by plan and forward kernels.  Keys come either as a used
+// prefix per segment (cu_k, used_k) or, in the key-range form (kr_off not
+// null), as the ranges kr_start[i] .. + kr_len[i], i in [kr_off[s],
+// kr_off[s + 1]), concatenated in order.
 struct Geometry {
   const int32_t* cu_q;
   const int32_t* cu_k;
   const int32_t* used_q;
   const int32_t* used_k;
+  const int32_t* kr_off;
+  const int32_t* kr_start;
+  const int32_t* kr_len;
+  int32_t nranges;
   int32_t nseg;
   int32_t total_q;
   int32_t total_k;
   int32_t hq;
   int32_t hkv;
-  int32_t d;
+  int32_t d;   // head dim of Q and K
+  int32_t dv;  // head dim of V and O
   int32_t causal;
 };
 
@@ -119,7 +132,7 @@ struct PlanArgs {
   int32_t max_tiles;   // capacity of the tile list
   uint32_t key;
   int64_t q_row_bytes;  // bytes of one packed Q/O row (all heads)
-  int64_t k_row_bytes;  // bytes of one packed K/V row (all heads)
+  int64_t k_row_bytes;  // bytes of one packed K or V row, the larger (all heads)
 };
 
 struct FwdArgs {
@@ -153,7 +166,8 @@ struct MergeArgs {
 
 // Host-side launchers (one translation unit each).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-// Matrix-core forward for 16-bit inputs (dtype GVATTN_BF16 or GVATTN_FP16).
+// Matrix-core forward for 16-bit inputs (dtype GVATTN_BF16 or GVATTN_FP16);
+// the key-range form when a.g.kr_off is set.
 hipError_t launch_fwd_mfma(const FwdArgs& a, int dtype, const TileShape& t, int64_t max_work,
                            hipStream_t s, bool* supported);
 hipError_t launch_fwd_fp32(const FwdArgs& a, const TileShape& t, int64_t max_work,

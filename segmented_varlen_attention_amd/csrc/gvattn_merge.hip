@@ -6,10 +6,13 @@
 //   m = max_p LSE_p;  m = -inf -> O = 0, LSE = -inf;
 //   else w_p = exp(LSE_p - m), W = sum_p w_p, LSE = m + ln W,
 //        O = sum_p (w_p / W) O_p.
-// The kernel is HBM-bound: D/8 lanes own one (row, head) and move it with
-// 16-byte vector loads/stores; consecutive (row, head) pairs are consecutive
-// rows of one head, so the LSE traffic is contiguous too.  Gap rows are
-// skipped (left untouched).  Each (row, head) is fully read before it is
+// The kernel is HBM-bound: D/32 lanes own one (row, head), 32 elements each,
+// moved with 16-byte vector loads/stores; the per-row work (segment lookup,
+// LSE loads, weights) is shared by few lanes.  Pairs are taken in row-major
+// order (all heads of a row, then the next row), which is the memory order
+// of O, so a block streams one contiguous piece of every partial and of the
+// output.
+// Gap rows are skipped (left untouched).  Each (row, head) is fully read before it is
 // written by the same lanes, so `out` may alias part_out[0].
 #include <math.h>
 
@@ -21,6 +24,7 @@ namespace {
 using namespace dev;
 
 constexpr int kThreads = 256;
+constexpr int kElems = 32;  // elements of one (row, head) per lane
 
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> {
@@ -89,8 +93,8 @@ __device__ __forceinline__ int find_segment(const int32_t* cu, int nseg, int row
 
 template <typename TIn, typename TOut, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  constexpr int LPP = D / 8;              // lanes per (row, head)
-  constexpr int PPB = kThreads / LPP;     // pairs per block per step
+  constexpr int LPP = D / kElems;          // lanes per (row, head)
+  constexpr int PPB = kThreads / LPP;      // pairs per block
   const int sub = threadIdx.x % LPP;
   const int slot = threadIdx.x / LPP;
   const int64_t npairs = (int64_t)a.hq * a.total_q;
@@ -106,67 +110,61 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     }
   }
 
-  for (int64_t base = (int64_t)blockIdx.x * PPB; base < npairs; base += (int64_t)gridDim.x * PPB) {
-    const int64_t pi = base + slot;
-    if (pi >= npairs) continue;
-    const int head = (int)(pi / a.total_q);
-    const int row = (int)(pi - (int64_t)head * a.total_q);
+  // pair = row * hq + head: the block's pairs are contiguous in O
+  const int64_t first = (int64_t)blockIdx.x * PPB;
+  if (first + slot >= npairs) return;
+  const int64_t row_first = first / a.hq;  // uniform
+  const int t = (int)(first - row_first * a.hq) + slot;
+  const int row = (int)(row_first + t / a.hq);
+  const int head = t % a.hq;
+  {
     const int s = find_segment(a.cu_q, a.nseg, row);
-    const int c0 = a.cu_q[s], c1 = a.cu_q[s + 1], u = a.used_q[s];
-    if (c0 < 0 || c1 < c0 || c1 > a.total_q || u < 0 || u > c1 - c0) continue;
-    if (row < c0 || row >= c0 + u) continue;
-
-    const int64_t lidx = (int64_t)head * a.total_q + row;
-    float L[GVATTN_MAX_PARTS];
-    float m = -INFINITY;
-    bool nan = false;
-#pragma unroll
-    for (int p = 0; p < GVATTN_MAX_PARTS; ++p) {
-      if (p < a.nparts) {
-        L[p] = a.part_lse[p][lidx];
-        nan |= (L[p] != L[p]);
-        m = fmaxf(m, L[p]);
-      }
-    }
-    const int64_t eoff = ((int64_t)row * a.hq + head) * D + sub * 8;
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    float lse_out;
-    if (nan) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = NAN;
-      lse_out = NAN;
-    } else if (m == -INFINITY) {
-      lse_out = -INFINITY;
-    } else {
-      constexpr float kLog2e = 1.4426950408889634f;
-      float wsum = 0.f;
-      float wp[GVATTN_MAX_PARTS];
-#pragma unroll
-      for (int p = 0; p < GVATTN_MAX_PARTS; ++p) {
-        wp[p] = 0.f;
-        if (p < a.nparts) {
-          wp[p] = __builtin_amdgcn_exp2f((L[p] - m) * kLog2e);
-          wsum += wp[p];
-        }
-      }
-      const float inv = 1.f / wsum;
-#pragma unroll
-      for (int p = 0; p < GVATTN_MAX_PARTS; ++p) {
-        if (p < a.nparts) {
-          float f[8];
-          Vec8<TIn>::load(static_cast<const TIn*>(a.part_out[p]) + eoff, f);
-          const float wn = wp[p] * inv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wn, f[i], acc[i]);
-        }
-      }
-      lse_out = m + logf(wsum);
-    }
-    Vec8<TOut>::store(static_cast<TOut*>(a.out) + eoff, acc);
-    if (sub == 0) a.lse[lidx] = lse_out;
+    const int c0 = a.cu_q[s], c1 = a.cu_q[s + 1], us = a.used_q[s];
+    if (c0 < 0 || c1 < c0 || c1 > a.total_q || us < 0 || us > c1 - c0) return;
+    if (row < c0 || row >= c0 + us) return;  // gap row: untouched
   }
+
+  const int64_t lidx = (int64_t)head * a.total_q + row;
+  float m = -INFINITY;
+  bool nan = false;
+  for (int p = 0; p < a.nparts; ++p) {
+    const float L = a.part_lse[p][lidx];
+    nan |= (L != L);
+    m = fmaxf(m, L);
+  }
+  const int64_t eoff = ((int64_t)row * a.hq + head) * D + sub * kElems;
+  float acc[kElems];
+#pragma unroll
+  for (int i = 0; i < kElems; ++i) acc[i] = 0.f;
+  float lse_out;
+  if (nan) {
+#pragma unroll
+    for (int i = 0; i < kElems; ++i) acc[i] = NAN;
+    lse_out = NAN;
+  } else if (m == -INFINITY) {
+    lse_out = -INFINITY;
+  } else {
+    constexpr float kLog2e = 1.4426950408889634f;
+    float wsum = 0.f;
+    for (int p = 0; p < a.nparts; ++p) {
+      const float w = __builtin_amdgcn_exp2f((a.part_lse[p][lidx] - m) * kLog2e);
+      const TIn* src = static_cast<const TIn*>(a.part_out[p]) + eoff;
+      float f[kElems];
+#pragma unroll
+      for (int c = 0; c < kElems / 8; ++c) Vec8<TIn>::load(src + 8 * c, f + 8 * c);
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < kElems; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int i = 0; i < kElems; ++i) acc[i] *= inv;
+    lse_out = m + logf(wsum);
+  }
+  TOut* dst = static_cast<TOut*>(a.out) + eoff;
+#pragma unroll
+  for (int c = 0; c < kElems / 8; ++c) Vec8<TOut>::store(dst + 8 * c, acc + 8 * c);
+  if (sub == 0) a.lse[lidx] = lse_out;
 }
 
 template <typename TIn, typename TOut>
@@ -179,10 +177,12 @@ hipError_t launch_t(const MergeArgs& a, hipStream_t s, bool* ok) {
     default: *ok = false; return hipSuccess;
   }
   *ok = true;
-  const int ppb = kThreads / (a.d / 8);
-  const int64_t need = ((int64_t)a.hq * a.total_q + ppb - 1) / ppb;
-  const int grid = persistent_grid(k, kThreads, need > 0 ? need : 1);
-  if (grid <= 0) return hipSuccess;
+  (void)k;
+  const int per_block = kThreads / (a.d / kElems);
+  const int64_t blocks = ((int64_t)a.hq * a.total_q + per_block - 1) / per_block;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int grid = (int)blocks;
   switch (a.d) {
     case 64: hipLaunchKernelGGL((merge_kernel<TIn, TOut, 64>), dim3(grid), dim3(kThreads), 0, s, a); break;
     case 128: hipLaunchKernelGGL((merge_kernel<TIn, TOut, 128>), dim3(grid), dim3(kThreads), 0, s, a); break;

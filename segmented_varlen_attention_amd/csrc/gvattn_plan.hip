@@ -4,7 +4,9 @@
 //
 // One workgroup of 1024 threads:
 //   1. validates every segment and counts its query tiles, ceil(used_q/R);
-//      an invalid segment gets no tiles and sets a device error bit;
+//      an invalid segment gets no tiles and sets a device error bit; in the
+//      key-range form it also sums the segment's range lengths (its key
+//      count) into the workspace;
 //   2. prefix-sums the counts into per-segment tile offsets;
 //   3. histograms the tiles by cost = number of 64-key tiles their rows see
 //      (under bottom-right causal the last row of the tile sees the most);
@@ -36,21 +38,47 @@ __device__ T block_exclusive_scan(T x, T* tmp, T* total) {
   return incl - x;
 }
 
+// Key-range form: checks segment s's ranges and returns their total length
+// in *keys (error bits, or 0).
+__device__ int range_error(const PlanArgs& a, int s, int* keys) {
+  const Geometry& g = a.g;
+  const int r0 = g.kr_off[s], r1 = g.kr_off[s + 1];
+  *keys = 0;
+  if (r0 < 0 || r1 < r0 || r1 > g.nranges) return GVATTN_DEVERR_KRANGES;
+  int64_t total = 0;
+  for (int i = r0; i < r1; ++i) {
+    const int st = g.kr_start[i], len = g.kr_len[i];
+    if (st < 0 || len < 0 || (int64_t)st + len > g.total_k) return GVATTN_DEVERR_KRANGES;
+    // a range's rows plus a tile of overrun stay below a 2^31-byte offset
+    if ((int64_t)(len + 256) * a.k_row_bytes >= (int64_t(1) << 31)) return GVATTN_DEVERR_RANGE;
+    total += len;
+  }
+  if (total >= (int64_t(1) << 31)) return GVATTN_DEVERR_KRANGES;
+  *keys = (int)total;
+  return 0;
+}
+
 __device__ int segment_error(const PlanArgs& a, int s) {
   const Geometry& g = a.g;
   const int cq0 = g.cu_q[s], cq1 = g.cu_q[s + 1];
-  const int ck0 = g.cu_k[s], ck1 = g.cu_k[s + 1];
-  const int uq = g.used_q[s], uk = g.used_k[s];
-  if (cq0 < 0 || cq1 < cq0 || cq1 > g.total_q || ck0 < 0 || ck1 < ck0 || ck1 > g.total_k)
-    return GVATTN_DEVERR_OFFSETS;
+  const int uq = g.used_q[s];
+  if (cq0 < 0 || cq1 < cq0 || cq1 > g.total_q) return GVATTN_DEVERR_OFFSETS;
   int err = 0;
   if (uq < 0 || uq > cq1 - cq0) err |= GVATTN_DEVERR_USED_Q;
-  if (uk < 0 || uk > ck1 - ck0) err |= GVATTN_DEVERR_USED_K;
   // Tiles may run up to 256 rows past a segment's capacity before the
   // bounds-checked loads reject them; keep every such offset below 2^31.
-  if ((int64_t)(cq1 - cq0 + 256) * a.q_row_bytes >= (int64_t(1) << 31) ||
-      (int64_t)(ck1 - ck0 + 256) * a.k_row_bytes >= (int64_t(1) << 31))
-    err |= GVATTN_DEVERR_RANGE;
+  if ((int64_t)(cq1 - cq0 + 256) * a.q_row_bytes >= (int64_t(1) << 31)) err |= GVATTN_DEVERR_RANGE;
+  if (g.kr_off != nullptr) {
+    int keys;
+    err |= range_error(a, s, &keys);
+    a.ws.seg_keys[s] = err ? 0 : keys;
+    return err;
+  }
+  const int ck0 = g.cu_k[s], ck1 = g.cu_k[s + 1];
+  const int uk = g.used_k[s];
+  if (ck0 < 0 || ck1 < ck0 || ck1 > g.total_k) return err | GVATTN_DEVERR_OFFSETS;
+  if (uk < 0 || uk > ck1 - ck0) err |= GVATTN_DEVERR_USED_K;
+  if ((int64_t)(ck1 - ck0 + 256) * a.k_row_bytes >= (int64_t(1) << 31)) err |= GVATTN_DEVERR_RANGE;
   return err;
 }
 
@@ -66,7 +94,8 @@ __device__ int find_segment(const int32_t* seg_off, int nseg, int t) {
 }
 
 __device__ int tile_bucket(const PlanArgs& a, int s, int row0) {
-  const int uq = a.g.used_q[s], uk = a.g.used_k[s];
+  const int uq = a.g.used_q[s];
+  const int uk = (a.g.kr_off != nullptr) ? a.ws.seg_keys[s] : a.g.used_k[s];
   int kend = uk;
   if (a.g.causal) {
     const int r_last = min(row0 + a.rows, uq) - 1;

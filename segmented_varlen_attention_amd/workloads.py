@@ -158,6 +158,8 @@ class Workload:
     v: np.ndarray  # [total_k, hkv, dv]
     partitions: list | None = None  # list of (cu_k, used_k) key partitions
     note: str = ""
+    # key-range form: (kr_off [nseg+1], kr_start [n], kr_len [n]) int32
+    key_ranges: tuple | None = None
 
     def out_init(self) -> np.ndarray:
         g = self.geom
@@ -279,11 +281,61 @@ def config5() -> Workload:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+def ulysses_joint(seed: int = 6, ranks: int = 2, text_cap: int = 4096, video: int = 4096,
+                  text_lens=(24, 700), nq: int = 4096, hq: int = 32, hkv: int = 8,
+                  d: int = 128, dtype: str = BF16) -> Workload:
+    """CFG batch of 2 under Ulysses sequence parallelism (issue #18687,
+    "Suggested fix" item 1): each sample's keys arrive rank-major, rank r
+    holding text rows [r*T/R, (r+1)*T/R) of the padded text and video rows
+    [r*V/R, (r+1)*V/R).  The valid keys of sample b are, per rank, the real
+    text rows of that chunk (text_lens[b] in total, pad slots exactly zero)
+    and the whole video chunk: 2*ranks key ranges per sample.  ``nq`` video
+    queries per sample attend them (non-causal)."""
+    tr, vr = text_cap // ranks, video // ranks
+    chunk = tr + vr
+    per_sample = ranks * chunk
+    nseg = len(text_lens)
+    g = make_geometry([nq] * nseg, [per_sample] * nseg, [nq] * nseg, [0] * nseg, hq, hkv, d,
+                      causal=False, dtype=dtype)
+    q, k, v = fill_qkv(g, seed)
+    starts, lens, off = [], [], [0]
+    for b, L in enumerate(text_lens):
+        base = b * per_sample
+        for r in range(ranks):
+            c0 = base + r * chunk
+            real = max(0, min(tr, L - r * tr))
+            k[c0 + real:c0 + tr] = 0.0
+            v[c0 + real:c0 + tr] = 0.0
+            starts += [c0, c0 + tr]
+            lens += [real, vr]
+        off.append(len(starts))
+    ranges = (np.asarray(off, np.int32), np.asarray(starts, np.int32),
+              np.asarray(lens, np.int32))
+    name = f"{dtype}_ulysses{ranks}_joint_b{nseg}_{nq}q_text{text_cap}_video{video}"
+    return Workload(name, seed, g, q, k, v, key_ranges=ranges,
+                    note="rank-major keys; pad-slot K/V exactly zero")
+
+
+def random_ranges(rng, nseg: int, total_k: int, max_ranges: int = 4, max_len: int = 80):
+    """Seeded key ranges for parity sweeps: 0..max_ranges ranges per segment,
+    lengths 0..max_len (some empty), starts anywhere in [0, total_k - len];
+    ranges may overlap and come in any order."""
+    counts = rng.integers(0, max_ranges + 1, size=nseg)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n = int(off[-1])
+    lens = rng.integers(0, max_len + 1, size=n)
+    lens[rng.random(n) < 0.15] = 0
+    lens = np.minimum(lens, total_k)
+    starts = np.array([rng.integers(0, total_k - L + 1) for L in lens], dtype=np.int64)
+    return off, starts.astype(np.int32), lens.astype(np.int32)
+
+
 def random_small(seed: int, nseg: int, cap_q: int, cap_k: int, hq: int, hkv: int,
                  d: int, causal: bool, dtype: str = BF16, lengths=None,
-                 std: float = 1.0) -> Workload:
+                 std: float = 1.0, dv: int | None = None) -> Workload:
     """Small seeded geometry for parity sweeps.  ``lengths`` may fix
-    (used_q, used_k); otherwise both are uniform in [0, cap]."""
+    (used_q, used_k); otherwise both are uniform in [0, cap].  ``dv`` is the
+    V/O head dim (default d)."""
     rng = np.random.default_rng(seed)
     if lengths is None:
         uq = rng.integers(0, cap_q, size=nseg, endpoint=True)
@@ -291,6 +343,6 @@ def random_small(seed: int, nseg: int, cap_q: int, cap_k: int, hq: int, hkv: int
     else:
         uq, uk = lengths
     g = make_geometry([cap_q] * nseg, [cap_k] * nseg, uq, uk, hq, hkv, d,
-                      causal=causal, dtype=dtype)
+                      causal=causal, dtype=dtype, dv=dv)
     q, k, v = fill_qkv(g, seed + 1000, std=std)
     return Workload(f"small_s{seed}", seed, g, q, k, v)

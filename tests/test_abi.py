@@ -32,6 +32,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for need in ("gvattn_fwd", "gvattn_lse_merge", "gvattn_fwd_plan", "gvattn_fwd_run",
+                 "gvattn_fwd_ranges",
                  "gvattn_fwd_workspace_size", "gvattn_status_string",
                  "gvattn_read_device_error", "gvattn_version"):
         assert need in names
@@ -74,7 +75,7 @@ def test_workspace_size(lib):
 def _fwd(lib, fn="gvattn_fwd", **over):
     args = dict(dtype=B.GVATTN_BF16, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE,
                 used_q=FAKE, used_k=FAKE, nseg=4, total_q=1024, total_k=1024, hq=8, hkv=2,
-                d=128, scale=0.125, causal=0, out=FAKE, lse=FAKE, ws=FAKE, ws_bytes=0,
+                d=128, dv=128, scale=0.125, causal=0, out=FAKE, lse=FAKE, ws=FAKE, ws_bytes=0,
                 stream=None)
     args.update(over)
     return getattr(lib, fn)(*args.values())
@@ -85,6 +86,8 @@ def test_fwd_host_validation(lib, fn):
     ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, B.GVATTN_BF16)
     assert _fwd(lib, fn, dtype=5, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
     assert _fwd(lib, fn, d=96, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _fwd(lib, fn, dv=96, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _fwd(lib, fn, dv=0, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
     assert _fwd(lib, fn, hkv=3, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
     assert _fwd(lib, fn, hq=0, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
     assert _fwd(lib, fn, nseg=-1, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
@@ -105,19 +108,48 @@ def test_fwd_host_validation(lib, fn):
 
 def test_plan_host_validation(lib):
     ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, B.GVATTN_BF16)
-    base = [B.GVATTN_BF16, FAKE, FAKE, FAKE, FAKE, 4, 1024, 1024, 8, 2, 128, 1, FAKE, ok_ws, None]
+    base = [B.GVATTN_BF16, FAKE, FAKE, FAKE, FAKE, 4, 1024, 1024, 8, 2, 128, 64, 1, FAKE, ok_ws,
+            None]
     bad = list(base)
     bad[10] = 80
+    assert lib.gvattn_fwd_plan(*bad) == B.GVATTN_ERR_UNSUPPORTED
+    bad = list(base)
+    bad[11] = 48
     assert lib.gvattn_fwd_plan(*bad) == B.GVATTN_ERR_UNSUPPORTED
     bad = list(base)
     bad[1] = None
     assert lib.gvattn_fwd_plan(*bad) == B.GVATTN_ERR_INVALID_ARG
     bad = list(base)
-    bad[13] = 16
+    bad[14] = 16
     assert lib.gvattn_fwd_plan(*bad) == B.GVATTN_ERR_WORKSPACE
     bad = list(base)
     bad[5] = 0
     assert lib.gvattn_fwd_plan(*bad) == B.GVATTN_OK
+
+
+def _fwd_ranges(lib, **over):
+    args = dict(dtype=B.GVATTN_BF16, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, used_q=FAKE,
+                kr_off=FAKE, kr_start=FAKE, kr_len=FAKE, nseg=4, nranges=9, total_q=1024,
+                total_k=1024, hq=8, hkv=2, d=128, dv=256, scale=0.125, causal=0, out=FAKE,
+                lse=FAKE, ws=FAKE, ws_bytes=0, stream=None)
+    args.update(over)
+    return lib.gvattn_fwd_ranges(*args.values())
+
+
+def test_fwd_ranges_host_validation(lib):
+    ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, B.GVATTN_BF16)
+    assert _fwd_ranges(lib, dtype=5, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _fwd_ranges(lib, d=96, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _fwd_ranges(lib, hkv=3, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    assert _fwd_ranges(lib, nranges=-1, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    assert _fwd_ranges(lib, causal=3, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    assert _fwd_ranges(lib, scale=0.0, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    for p in ("q", "k", "v", "cu_q", "used_q", "kr_off", "kr_start", "kr_len", "out", "lse"):
+        assert _fwd_ranges(lib, ws_bytes=ok_ws, **{p: None}) == B.GVATTN_ERR_INVALID_ARG, p
+    assert _fwd_ranges(lib, ws_bytes=ok_ws - 1) == B.GVATTN_ERR_WORKSPACE
+    assert _fwd_ranges(lib, ws=FAKE + 16, ws_bytes=ok_ws) == B.GVATTN_ERR_WORKSPACE
+    # no ranges at all needs no range arrays (validation only: nseg = 0)
+    assert _fwd_ranges(lib, nseg=0, nranges=0, kr_start=None, kr_len=None) == B.GVATTN_OK
 
 
 def test_merge_host_validation(lib):

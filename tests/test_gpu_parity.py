@@ -34,13 +34,13 @@ EDGE_Q = [0, 1, 31, 32, 33, 70, 96]
 EDGE_K = [0, 1, 63, 64, 65, 129, 160]
 
 
-def small_case(seed, g, d, causal, dtype, hkv=2):
+def small_case(seed, g, d, causal, dtype, hkv=2, dv=None):
     rng = np.random.default_rng(seed)
     nseg = 7
     uq = rng.permutation(EDGE_Q)[:nseg]
     uk = rng.permutation(EDGE_K)[:nseg]
     return W.random_small(seed, nseg, 96, 160, g * hkv, hkv, d, causal, dtype,
-                          lengths=(uq, uk))
+                          lengths=(uq, uk), dv=dv)
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
@@ -65,6 +65,20 @@ def test_small_fp16(d, g, causal):
     dc = DeviceCase(wl)
     out, lse, _ = dc.fwd()
     st = compare_full(out, lse, wl, where=f"fp16 d{d} g{g} c{int(causal)}", derived=True)
+    say("   ", st)
+
+
+@pytest.mark.parametrize("d,dv", [(128, 64), (64, 128), (256, 128), (128, 256), (64, 256),
+                                  (256, 64)])
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP32])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_dv(d, dv, dtype, causal):
+    """V/O head dim different from the Q/K one (the pages' FA2 path takes
+    equal dims only; the rest goes to their FP32 fallback)."""
+    wl = small_case(170 + d + dv, 4, d, causal, dtype, dv=dv)
+    say(f"[small dv] {dtype} d={d} dv={dv} causal={causal}")
+    out, lse, _ = DeviceCase(wl).fwd()
+    st = compare_full(out, lse, wl, where=f"{dtype} d{d} dv{dv} c{int(causal)}", derived=True)
     say("   ", st)
 
 
