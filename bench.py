@@ -10,7 +10,9 @@ head; masked, gap and padding work is never counted.
 Prints one JSON line.  ``--config N`` benches another workload (2, 4, 5:
 4 times the two partition launches plus the LSE merge, or with ``--fused``
 one key-range launch over both partitions; 6: the Ulysses rank-major joint
-attention of issue #18687 through the key-range entry point);
+attention of issue #18687 through the key-range entry point; 7: a
+decode-like batch that the plan splits along the keys, reported against
+the HBM roofline);
 ``--dtype fp16`` runs the same workload through the fp16 matrix-core path
 (the bf16-exact draws converted to fp16).
 """
@@ -99,7 +101,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5, 6, 7])
     ap.add_argument("--fused", action="store_true",
                     help="config 4: both partitions as key ranges of one launch")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
@@ -138,7 +140,8 @@ def main():
         return
 
     t0 = time.time()
-    wl = W.ulysses_joint() if args.config == 6 else W.CONFIGS[args.config]()
+    wl = (W.ulysses_joint() if args.config == 6 else
+          W.decode_batch() if args.config == 7 else W.CONFIGS[args.config]())
     g = wl.geom
     fused = args.config == 4 and args.fused
     if fused:
@@ -180,16 +183,16 @@ def main():
         kr = tuple(up(x) for x in wl.key_ranges)
         launches = []
         parts = [(out, lse)]
-        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode)]
+        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode, d_v=g.dv)]
     elif args.config == 4:
         launches = [(up(cu), up(u)) for cu, u in wl.partitions]
         parts = [(torch.empty_like(out), torch.empty_like(lse)) for _ in launches]
-        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode)
+        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode, d_v=g.dv)
                for _ in launches]
     else:
         launches = [(up(g.cu_k), up(g.used_k))]
         parts = [(out, lse)]
-        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode)]
+        wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode, d_v=g.dv)]
 
     def step():
         if wl.key_ranges is not None:
@@ -266,11 +269,16 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": (traffic_rec["bytes_per_launch"] if traffic_rec else None)}
+    if args.config == 7:  # memory-bound: algorithmic bytes over the whole call
+        gbs = algorithmic_bytes(g) / (kern_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
     names = {2: "bf16_cfg_cross_attn_b2_4096q_text24_700_gqa32x8_d128",
              3: "bf16_causal_gapped_replay_64x2048_gqa32x8_d128",
              4: "bf16_multiview_8x8190q_32760k_2partitions_merge_gqa24x8_d128",
              5: "bf16_gapped_16x16384_gqa16x4_d256",
-             6: "bf16_ulysses2_rank_major_joint_b2_4096q_text4096_video4096_keyranges"}
+             6: "bf16_ulysses2_rank_major_joint_b2_4096q_text4096_video4096_keyranges",
+             7: "bf16_decode_b32x4_k4096_16384_gqa32x8_d128_causal_splitk"}
     res = {
         "metric": "gapped varlen attn fwd TFLOP/s (used rows) + % of MI355X bf16 MFMA peak",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -93,11 +93,15 @@ typedef enum gvattn_dtype {
 
 /*
  * Bytes of device workspace gvattn_fwd needs for this geometry: a plan
- * header, the tile work list and per-segment offsets.  It depends only on the
- * host-known sizes, never on device data.  Returns 0 for invalid arguments.
+ * header, the work list and per-segment offsets, and, for launches with few
+ * query tiles (fewer than 512 tiles x head groups, 16-bit types), room for
+ * FP32 split-K partials: up to 16 chunks of [total_q, hq, d_v] plus their
+ * LSE, 64 MiB at most.  It depends only on the host-known sizes, never on
+ * device data.
+ * Returns 0 for invalid arguments.
  */
 size_t gvattn_fwd_workspace_size(int32_t nseg, int32_t total_q, int32_t hq,
-                                 int32_t hkv, int32_t d, int32_t dtype);
+                                 int32_t hkv, int32_t d, int32_t d_v, int32_t dtype);
 
 /*
  * Segmented varlen attention forward: plan + run (PR #302, "What").

@@ -44,7 +44,7 @@ _FWD_ARGS = [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i
              _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp]
 
 SIGNATURES = {
-    "gvattn_fwd_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "gvattn_fwd_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "gvattn_fwd": (ctypes.c_int, _FWD_ARGS),
     "gvattn_fwd_run": (ctypes.c_int, _FWD_ARGS),
     "gvattn_fwd_plan": (ctypes.c_int, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -152,14 +152,16 @@ def _fwd_common(q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, 
 
 
 def gvattn_fwd_workspace_size(nseg: int, total_q: int, hq: int, hkv: int, d: int,
-                              dtype: int) -> int:
-    return int(load_library().gvattn_fwd_workspace_size(nseg, total_q, hq, hkv, d, dtype))
+                              dtype: int, d_v: int | None = None) -> int:
+    return int(load_library().gvattn_fwd_workspace_size(nseg, total_q, hq, hkv, d,
+                                                        d if d_v is None else d_v, dtype))
 
 
-def alloc_workspace(nseg: int, total_q: int, hq: int, hkv: int, d: int, dtype: int, device=None):
+def alloc_workspace(nseg: int, total_q: int, hq: int, hkv: int, d: int, dtype: int, device=None,
+                    d_v: int | None = None):
     """Device workspace for gvattn_fwd (torch's allocator aligns to 512 B)."""
     torch = _torch()
-    n = gvattn_fwd_workspace_size(nseg, total_q, hq, hkv, d, dtype)
+    n = gvattn_fwd_workspace_size(nseg, total_q, hq, hkv, d, dtype, d_v)
     if n == 0:
         raise ValueError("invalid geometry for a workspace")
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
@@ -171,7 +173,7 @@ def _fwd_call(fn_name, q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k
         q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, lse)
     dt = _dtype_code(q)
     if workspace is None:
-        workspace = alloc_workspace(nseg, total_q, hq, hkv, d, dt, q.device)
+        workspace = alloc_workspace(nseg, total_q, hq, hkv, d, dt, q.device, dv)
     lib = load_library()
     rc = getattr(lib, fn_name)(
         dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
@@ -214,7 +216,7 @@ def gvattn_fwd_ranges(q, k, v, cu_seqlens_q, seqused_q, kr_off, kr_start, kr_len
     _check_i32_vec(kr_len, nranges, "kr_len")
     dt = _dtype_code(q)
     if workspace is None:
-        workspace = alloc_workspace(nseg, total_q, hq, hkv, d, dt, q.device)
+        workspace = alloc_workspace(nseg, total_q, hq, hkv, d, dt, q.device, dv)
     rc = load_library().gvattn_fwd_ranges(
         dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
         seqused_q.data_ptr(), kr_off.data_ptr(),
@@ -237,7 +239,7 @@ def gvattn_fwd_plan(dtype: int, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k
     _check_i32_vec(seqused_q, nseg, "seqused_q")
     _check_i32_vec(seqused_k, nseg, "seqused_k")
     if workspace is None:
-        workspace = alloc_workspace(nseg, total_q, hq, hkv, d, dtype, seqused_q.device)
+        workspace = alloc_workspace(nseg, total_q, hq, hkv, d, dtype, seqused_q.device, d_v)
     rc = load_library().gvattn_fwd_plan(
         dtype, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), seqused_q.data_ptr(),
         seqused_k.data_ptr(), nseg, total_q, total_k, hq, hkv, d, d if d_v is None else d_v,

@@ -82,12 +82,20 @@ int check_sizes(int32_t dtype, int32_t nseg, int32_t total_q, int32_t total_k, i
   return GVATTN_OK;
 }
 
-int check_workspace(const void* ws, size_t bytes, int32_t nseg, int32_t total_q, int rows) {
+WsLayout layout_of(int32_t dtype, int32_t nseg, int32_t total_q, int32_t hq, int32_t hkv,
+                   int32_t d, int32_t dv) {
+  return ws_layout(nseg, total_q, hq, dv, choose_shape(dtype, hq, hkv, d), dtype);
+}
+
+int check_workspace(const void* ws, size_t bytes, const WsLayout& L) {
   if (ws == nullptr) return GVATTN_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % GVATTN_WORKSPACE_ALIGN != 0) return GVATTN_ERR_WORKSPACE;
-  if (bytes < workspace_bytes(nseg, total_q, rows)) return GVATTN_ERR_WORKSPACE;
+  if (bytes < L.bytes) return GVATTN_ERR_WORKSPACE;
   return GVATTN_OK;
 }
+
+// keys per key tile of the forward kernel (split-K chunks are whole tiles)
+int key_tile(int32_t d, int32_t dv) { return (d <= 128 && dv <= 128) ? 32 : 64; }
 
 Geometry make_geom(const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
                    const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
@@ -114,11 +122,14 @@ Geometry make_geom(const int32_t* cu_q, const int32_t* cu_k, const int32_t* used
 
 int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
   const TileShape t = choose_shape(dtype, g.hq, g.hkv, g.d);
+  const WsLayout L = layout_of(dtype, g.nseg, g.total_q, g.hq, g.hkv, g.d, g.dv);
   PlanArgs a;
   a.g = g;
-  a.ws = view_workspace(ws, g.nseg, g.total_q, t.rows);
+  a.ws = view_workspace(ws, L);
   a.rows = t.rows;
-  a.max_tiles = (int32_t)max_tiles(g.nseg, g.total_q, t.rows);
+  a.max_tiles = (int32_t)L.max_tiles;
+  a.key_tile = key_tile(g.d, g.dv);
+  a.n_head_chunks = g.hq / t.gf;
   a.key = plan_key(t.rows, g.causal, g.nseg, (g.kr_off != nullptr) | (g.d << 1) | (g.dv << 10));
   const int dmax = g.d > g.dv ? g.d : g.dv;
   a.q_row_bytes = (int64_t)g.hq * dmax * esize(dtype);
@@ -129,9 +140,10 @@ int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
 int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const void* v,
            float scale, void* out, float* lse, void* ws, hipStream_t stream) {
   const TileShape t = choose_shape(dtype, g.hq, g.hkv, g.d);
+  const WsLayout L = layout_of(dtype, g.nseg, g.total_q, g.hq, g.hkv, g.d, g.dv);
   FwdArgs a;
   a.g = g;
-  a.ws = view_workspace(ws, g.nseg, g.total_q, t.rows);
+  a.ws = view_workspace(ws, L);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -140,11 +152,12 @@ int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   a.scale_log2 = scale * kLog2e;
   a.key = plan_key(t.rows, g.causal, g.nseg, (g.kr_off != nullptr) | (g.d << 1) | (g.dv << 10));
   a.n_head_chunks = g.hq / t.gf;
-  const int64_t max_work = max_tiles(g.nseg, g.total_q, t.rows) * a.n_head_chunks;
+  const int64_t max_work = L.max_tiles * L.splits * a.n_head_chunks;
   bool ok = false;
   hipError_t e = (dtype != GVATTN_FP32) ? launch_fwd_mfma(a, dtype, t, max_work, stream, &ok)
                                         : launch_fwd_fp32(a, t, max_work, stream, &ok);
   if (!ok) return GVATTN_ERR_UNSUPPORTED;
+  if (e == hipSuccess && L.splits > 1) e = launch_split_merge(a, dtype, stream);
   return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
 }
 
@@ -159,8 +172,7 @@ int check_fwd_args(int32_t dtype, const void* q, const void* k, const void* v,
   if (nseg == 0) return GVATTN_OK;
   if (!q || !k || !v || !cu_q || !cu_k || !used_q || !used_k || !out || !lse)
     return GVATTN_ERR_INVALID_ARG;
-  const TileShape t = choose_shape(dtype, hq, hkv, d);
-  return check_workspace(ws, ws_bytes, nseg, total_q, t.rows);
+  return check_workspace(ws, ws_bytes, layout_of(dtype, nseg, total_q, hq, hkv, d, dv));
 }
 
 }  // namespace
@@ -171,10 +183,9 @@ using namespace gvattn;
 extern "C" {
 
 size_t gvattn_fwd_workspace_size(int32_t nseg, int32_t total_q, int32_t hq, int32_t hkv,
-                                 int32_t d, int32_t dtype) {
-  if (check_sizes(dtype, nseg, total_q, 0, hq, hkv, d, d, 0) != GVATTN_OK) return 0;
-  const TileShape t = choose_shape(dtype, hq, hkv, d);
-  return workspace_bytes(nseg, total_q, t.rows);
+                                 int32_t d, int32_t d_v, int32_t dtype) {
+  if (check_sizes(dtype, nseg, total_q, 0, hq, hkv, d, d_v, 0) != GVATTN_OK) return 0;
+  return layout_of(dtype, nseg, total_q, hq, hkv, d, d_v).bytes;
 }
 
 int gvattn_fwd_plan(int32_t dtype, const int32_t* cu_q, const int32_t* cu_k,
@@ -186,8 +197,8 @@ int gvattn_fwd_plan(int32_t dtype, const int32_t* cu_q, const int32_t* cu_k,
   if (rc != GVATTN_OK) return rc;
   if (nseg == 0) return GVATTN_OK;
   if (!cu_q || !cu_k || !used_q || !used_k) return GVATTN_ERR_INVALID_ARG;
-  const TileShape t = choose_shape(dtype, hq, hkv, d);
-  rc = check_workspace(workspace, workspace_bytes_, nseg, total_q, t.rows);
+  rc = check_workspace(workspace, workspace_bytes_,
+                       layout_of(dtype, nseg, total_q, hq, hkv, d, d_v));
   if (rc != GVATTN_OK) return rc;
   const Geometry g =
       make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
@@ -244,8 +255,8 @@ int gvattn_fwd_ranges(int32_t dtype, const void* q, const void* k, const void* v
   if (nseg == 0) return GVATTN_OK;
   if (!q || !k || !v || !cu_q || !used_q || !kr_off || !out || !lse) return GVATTN_ERR_INVALID_ARG;
   if (nranges > 0 && (!kr_start || !kr_len)) return GVATTN_ERR_INVALID_ARG;
-  const TileShape t = choose_shape(dtype, hq, hkv, d);
-  rc = check_workspace(workspace, workspace_bytes_, nseg, total_q, t.rows);
+  rc = check_workspace(workspace, workspace_bytes_,
+                       layout_of(dtype, nseg, total_q, hq, hkv, d, d_v));
   if (rc != GVATTN_OK) return rc;
   Geometry g = make_geom(cu_q, nullptr, used_q, nullptr, nseg, total_q, total_k, hq, hkv, d,
                          d_v, causal);

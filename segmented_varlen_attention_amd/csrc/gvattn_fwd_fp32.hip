@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(FwdArgs a, int rows_
     const int t = (int)(w / hq);
     const int head = (int)(w - (int64_t)t * hq);
     const int kvh = head / G;
-    const int2 tile = a.ws.tiles[t];
+    const int4 tile = a.ws.tiles[t];  // never split: all key tiles
     const int seg = tile.x, row0 = tile.y;
     // keys: the used prefix at k0, or the segment's ranges concatenated
     const bool kr = a.g.kr_off != nullptr;

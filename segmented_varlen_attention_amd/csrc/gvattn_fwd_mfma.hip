@@ -235,7 +235,7 @@ void fwd_mfma_kernel(FwdArgs a) {
     const int hc = w - t * n_hc;
     // Work-item geometry is wave-uniform: keep it in scalar registers so
     // the buffer resources built from it need no per-lane loops.
-    const int2 tile = a.ws.tiles[t];
+    const int4 tile = a.ws.tiles[t];
     const int seg = __builtin_amdgcn_readfirstlane(tile.x);
     const int row0 = __builtin_amdgcn_readfirstlane(tile.y);
     const int head0 = hc * GF;
@@ -288,6 +288,12 @@ void fwd_mfma_kernel(FwdArgs a) {
     } else {
       n_kt = (kend + C::BN - 1) / C::BN;
     }
+    // key tiles of this entry: all of them, or one split-K chunk
+    // [tile.z, tile.w >> 5) whose result goes to the FP32 partials
+    const bool partial = !KR && (tile.w & 1);
+    const int split_j = (tile.w >> 1) & 15;
+    const int kt_begin = KR ? 0 : min(__builtin_amdgcn_readfirstlane(tile.z), n_kt);
+    const int kt_end = KR ? n_kt : min(__builtin_amdgcn_readfirstlane(tile.w) >> 5, n_kt);
 
     const T* qbase = static_cast<const T*>(a.q) + ((int64_t)q0 * a.g.hq + head) * DQ;
     const uint32_t qbytes = uq > 0 ? (uint32_t)(uq - 1) * qstride + DQ * 2 : 0u;
@@ -321,7 +327,7 @@ void fwd_mfma_kernel(FwdArgs a) {
       }
     };
 
-    if (n_kt > 0) issue_tile(0);
+    if (kt_begin < kt_end) issue_tile(kt_begin);
 
     // Q fragment: lane holds Q[wr0 + r32][16*kk + 8*hh .. +7]
     v8 qf[C::KK];
@@ -342,7 +348,7 @@ void fwd_mfma_kernel(FwdArgs a) {
     const int lim_w = a.g.causal ? min(uk, wr0 + uk - uq + 1) : uk;  // wave minimum
 
     KeyCursor nx = cur;
-    for (int kt = 0; kt < n_kt; ++kt) {
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
       wait_vmem();
       __syncthreads();
       const char* Ks = lds + (kt & 1) * C::STAGE_BYTES;
@@ -353,7 +359,7 @@ void fwd_mfma_kernel(FwdArgs a) {
       // their issue overlaps matrix-core work.  Without a next tile they go
       // through zero-size buffer resources (every load returns zero into the
       // stage nobody reads any more), which keeps the phase branch-free.
-      const int nlen = (kt + 1 < n_kt) ? (KR ? nx.len : uk) : 0;
+      const int nlen = (kt + 1 < kt_end) ? (KR ? nx.len : uk) : 0;
       const int nfirst = KR ? nx.row0 : k0;
       const auto krn = k_rsrc(nfirst, nlen);
       const auto vrn = v_rsrc(nfirst, nlen);
@@ -473,10 +479,30 @@ void fwd_mfma_kernel(FwdArgs a) {
     const float l_tot = sum_across_halves(l_run);
     const bool dead = (l_tot == 0.f);
     const float inv = dead ? 0.f : 1.f / l_tot;
-    if (hh == 0 && row < uq) {
-      const float lse = dead ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
-      a.lse[(int64_t)head * a.g.total_q + q0 + row] = lse;
+    const float lse = dead ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+    if (partial) {
+      // split-K chunk: FP32 O (normalised over the chunk) and LSE of chunk
+      // split_j, straight from the registers
+      if (row < uq) {
+        float* po = a.ws.part_o +
+                    (((int64_t)split_j * a.g.total_q + q0 + row) * a.g.hq + head) * DV;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            f32x4 ov;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) ov[cc] = o[db][4 * a4 + cc] * inv;
+            *reinterpret_cast<f32x4*>(po + db * 32 + 8 * a4 + 4 * hh) = ov;
+          }
+        if (hh == 0)
+          a.ws.part_lse[((int64_t)split_j * a.g.hq + head) * a.g.total_q + q0 + row] = lse;
+      }
+      wait_vmem();      // loads past the last tile still write their stage
+      __syncthreads();  // the next item's K/V loads reuse the stages
+      continue;
     }
+    if (hh == 0 && row < uq) a.lse[(int64_t)head * a.g.total_q + q0 + row] = lse;
     __syncthreads();  // every wave is done with the K/V stages
     T* Os = reinterpret_cast<T*>(lds) + wave * 32 * C::OP;
 #pragma unroll

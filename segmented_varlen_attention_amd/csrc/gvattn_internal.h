@@ -10,24 +10,40 @@
 namespace gvattn {
 
 // ---------------------------------------------------------------------------
-// Workspace: [PlanHeader (256 B)] [tile list: int2 x max_tiles]
-//            [per-segment tile offsets: int32 x (nseg + 1)]
+// Workspace: [PlanHeader (256 B)]
+//            [work list: int4 x max_tiles * splits]
+//            [per-segment work offsets: int32 x (nseg + 1)]
 //            [per-segment key count: int32 x (nseg + 1)] (key-range form)
-// A tile is (segment, first row in the segment); the list is sorted by
-// decreasing number of key tiles so that the persistent kernel takes the
-// longest work first.
+//            [per-segment split count: int32 x (nseg + 1)]
+//            [split partials, only when splits > 1:
+//               O fp32 [splits][total_q][hq][d_v], LSE fp32 [splits][hq][total_q]]
+// A work entry is (segment, first row, first key tile, end key tile * 32 +
+// split index * 2 + partial flag): one query tile, or one key chunk of it
+// when the problem has too few query tiles to fill the GPU.  The list is
+// sorted by decreasing number of key tiles so that the persistent kernel
+// takes the longest work first.
 // ---------------------------------------------------------------------------
 struct PlanHeader {
-  int32_t n_tiles;
+  int32_t n_tiles;        // work entries
   int32_t err;
   uint32_t key;
   int32_t rows_per_tile;
-  int32_t reserved[60];
+  int32_t max_split;      // most chunks any query tile was split into
+  int32_t reserved[59];
 };
 static_assert(sizeof(PlanHeader) == 256, "plan header is 256 bytes");
 
-constexpr int kKeyTile = 64;          // keys per LDS tile (BN)
-constexpr int kCostBuckets = 2048;    // sort buckets (key tiles per q-tile)
+constexpr int kCostBuckets = 2048;    // sort buckets (key tiles per entry)
+
+// Split-K: a launch with fewer than kSplitBelow work items (query tiles x
+// head chunks) may split long key ranges into up to `splits` chunks of at
+// least kMinSplitTiles key tiles, aiming at about kSplitAim items; the
+// chunks write FP32 partials that a merge pass combines.
+constexpr int kSplitBelow = 512;
+constexpr int kSplitAim = 2048;
+constexpr int kMaxSplits = 16;
+constexpr int kMinSplitTiles = 8;
+constexpr int64_t kSplitBytes = int64_t(64) << 20;  // partials at most
 
 // Tile shape of one forward variant.
 struct TileShape {
@@ -75,30 +91,67 @@ inline int64_t max_tiles(int64_t nseg, int64_t total_q, int rows) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline size_t workspace_bytes(int64_t nseg, int64_t total_q, int rows) {
+// Byte layout of the workspace; a function of host-known sizes only.
+struct WsLayout {
+  int64_t max_tiles;  // query tiles at most
+  int32_t splits;     // key chunks per query tile at most (1: no split-K)
+  size_t tiles, seg_off, seg_keys, seg_split, part_o, part_lse, bytes;
+};
+
+inline WsLayout ws_layout(int64_t nseg, int64_t total_q, int hq, int dv, const TileShape& t,
+                          int dtype) {
+  WsLayout L{};
+  L.max_tiles = max_tiles(nseg, total_q, t.rows);
+  const int64_t items = L.max_tiles * (hq / t.gf);
+  L.splits = 1;
+  if (dtype != GVATTN_FP32 && items < kSplitBelow) {
+    int64_t s = (kSplitAim + items - 1) / items;
+    const int64_t per_split = (int64_t)total_q * hq * (dv + 1) * 4;
+    if (per_split > 0 && s * per_split > kSplitBytes) s = kSplitBytes / per_split;
+    L.splits = (int32_t)(s < 1 ? 1 : (s < kMaxSplits ? s : kMaxSplits));
+  }
   size_t b = sizeof(PlanHeader);
-  b += align_up((size_t)max_tiles(nseg, total_q, rows) * 8, 256);
-  b += 2 * align_up((size_t)(nseg + 1) * 4, 256);
-  return b;
+  L.tiles = b;
+  b += align_up((size_t)L.max_tiles * L.splits * 16, 256);
+  L.seg_off = b;
+  b += align_up((size_t)(nseg + 1) * 4, 256);
+  L.seg_keys = b;
+  b += align_up((size_t)(nseg + 1) * 4, 256);
+  L.seg_split = b;
+  b += align_up((size_t)(nseg + 1) * 4, 256);
+  L.part_o = L.part_lse = 0;
+  if (L.splits > 1) {
+    L.part_o = b;
+    b += align_up((size_t)L.splits * total_q * hq * dv * 4, 256);
+    L.part_lse = b;
+    b += align_up((size_t)L.splits * hq * total_q * 4, 256);
+  }
+  L.bytes = b;
+  return L;
 }
 
 struct WorkspaceView {
   PlanHeader* header;
-  int2* tiles;
+  int4* tiles;
   int32_t* seg_tile_off;
-  int32_t* seg_keys;  // key-range form: total key count of each segment
+  int32_t* seg_keys;   // key-range form: total key count of each segment
+  int32_t* seg_split;  // key chunks each query tile of the segment is split into
+  float* part_o;       // split partials (null without split-K)
+  float* part_lse;
+  int32_t splits;      // capacity: most chunks per query tile
 };
 
-inline WorkspaceView view_workspace(void* ws, int64_t nseg, int64_t total_q, int rows) {
+inline WorkspaceView view_workspace(void* ws, const WsLayout& L) {
   WorkspaceView v;
   char* p = static_cast<char*>(ws);
   v.header = reinterpret_cast<PlanHeader*>(p);
-  p += sizeof(PlanHeader);
-  v.tiles = reinterpret_cast<int2*>(p);
-  p += align_up((size_t)max_tiles(nseg, total_q, rows) * 8, 256);
-  v.seg_tile_off = reinterpret_cast<int32_t*>(p);
-  p += align_up((size_t)(nseg + 1) * 4, 256);
-  v.seg_keys = reinterpret_cast<int32_t*>(p);
+  v.tiles = reinterpret_cast<int4*>(p + L.tiles);
+  v.seg_tile_off = reinterpret_cast<int32_t*>(p + L.seg_off);
+  v.seg_keys = reinterpret_cast<int32_t*>(p + L.seg_keys);
+  v.seg_split = reinterpret_cast<int32_t*>(p + L.seg_split);
+  v.part_o = L.splits > 1 ? reinterpret_cast<float*>(p + L.part_o) : nullptr;
+  v.part_lse = L.splits > 1 ? reinterpret_cast<float*>(p + L.part_lse) : nullptr;
+  v.splits = L.splits;
   return v;
 }
 
@@ -129,7 +182,9 @@ struct PlanArgs {
   Geometry g;
   WorkspaceView ws;
   int32_t rows;        // rows per tile
-  int32_t max_tiles;   // capacity of the tile list
+  int32_t max_tiles;   // query tiles at most (the list holds max_tiles * splits)
+  int32_t key_tile;    // keys per key tile of the forward kernel
+  int32_t n_head_chunks;
   uint32_t key;
   int64_t q_row_bytes;  // bytes of one packed Q/O row (all heads)
   int64_t k_row_bytes;  // bytes of one packed K or V row, the larger (all heads)
@@ -166,6 +221,9 @@ struct MergeArgs {
 
 // Host-side launchers (one translation unit each).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+// Combines the split-K partials of the segments the plan split (dtype of
+// the output: GVATTN_BF16 or GVATTN_FP16).
+hipError_t launch_split_merge(const FwdArgs& a, int dtype, hipStream_t s);
 // Matrix-core forward for 16-bit inputs (dtype GVATTN_BF16 or GVATTN_FP16);
 // the key-range form when a.g.kr_off is set.
 hipError_t launch_fwd_mfma(const FwdArgs& a, int dtype, const TileShape& t, int64_t max_work,

@@ -191,6 +191,78 @@ hipError_t launch_t(const MergeArgs& a, hipStream_t s, bool* ok) {
   return hipGetLastError();
 }
 
+// Split-K merge: for every used row of a segment the plan split into S > 1
+// key chunks, combine the chunks' FP32 partials (O over the chunk, LSE of
+// the chunk) exactly as the LSE merge combines partitions, into out / lse.
+template <typename TOut, int D>
+__global__ __launch_bounds__(kThreads) void split_merge_kernel(FwdArgs a) {
+  constexpr int LPP = D / kElems;
+  constexpr int PPB = kThreads / LPP;
+  const PlanHeader* hdr = a.ws.header;
+  if (hdr->key != a.key || hdr->n_tiles == 0 || hdr->max_split <= 1) return;
+  const int sub = threadIdx.x % LPP;
+  const int slot = threadIdx.x / LPP;
+  const int hq = a.g.hq, total_q = a.g.total_q;
+  const int64_t npairs = (int64_t)hq * total_q;
+  const int64_t first = (int64_t)blockIdx.x * PPB;
+  if (first + slot >= npairs) return;
+  const int64_t row_first = first / hq;
+  const int t = (int)(first - row_first * hq) + slot;
+  const int row = (int)(row_first + t / hq);
+  const int head = t % hq;
+  const int s = find_segment(a.g.cu_q, a.g.nseg, row);
+  const int S = a.ws.seg_split[s];
+  if (S <= 1) return;
+  const int c0 = a.g.cu_q[s], us = a.g.used_q[s];
+  if (row < c0 || row >= c0 + us) return;
+
+  float m = -INFINITY;
+  for (int j = 0; j < S; ++j)
+    m = fmaxf(m, a.ws.part_lse[((int64_t)j * hq + head) * total_q + row]);
+  float acc[kElems];
+#pragma unroll
+  for (int i = 0; i < kElems; ++i) acc[i] = 0.f;
+  float lse_out = -INFINITY;
+  if (m != -INFINITY) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    float wsum = 0.f;
+    for (int j = 0; j < S; ++j) {
+      const float L = a.ws.part_lse[((int64_t)j * hq + head) * total_q + row];
+      const float w = __builtin_amdgcn_exp2f((L - m) * kLog2e);
+      const float* src = a.ws.part_o + (((int64_t)j * total_q + row) * hq + head) * D + sub * kElems;
+      float f[kElems];
+#pragma unroll
+      for (int c = 0; c < kElems / 8; ++c) Vec8<float>::load(src + 8 * c, f + 8 * c);
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < kElems; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int i = 0; i < kElems; ++i) acc[i] *= inv;
+    lse_out = m + logf(wsum);
+  }
+  TOut* dst = static_cast<TOut*>(a.out) + ((int64_t)row * hq + head) * D + sub * kElems;
+#pragma unroll
+  for (int c = 0; c < kElems / 8; ++c) Vec8<TOut>::store(dst + 8 * c, acc + 8 * c);
+  if (sub == 0) a.lse[(int64_t)head * total_q + row] = lse_out;
+}
+
+template <typename TOut>
+hipError_t launch_split_t(const FwdArgs& a, hipStream_t s) {
+  const int per_block = kThreads / (a.g.dv / kElems);
+  const int64_t blocks = ((int64_t)a.g.hq * a.g.total_q + per_block - 1) / per_block;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  switch (a.g.dv) {
+    case 64: hipLaunchKernelGGL((split_merge_kernel<TOut, 64>), dim3((int)blocks), dim3(kThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((split_merge_kernel<TOut, 128>), dim3((int)blocks), dim3(kThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((split_merge_kernel<TOut, 256>), dim3((int)blocks), dim3(kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int part_dtype, int out_dtype, hipStream_t s,
@@ -209,6 +281,12 @@ hipError_t launch_merge(const MergeArgs& a, int part_dtype, int out_dtype, hipSt
   }
   *supported = false;
   return hipSuccess;
+}
+
+hipError_t launch_split_merge(const FwdArgs& a, int dtype, hipStream_t s) {
+  if (dtype == GVATTN_BF16) return launch_split_t<__bf16>(a, s);
+  if (dtype == GVATTN_FP16) return launch_split_t<_Float16>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gvattn

@@ -8,10 +8,13 @@
 //      key-range form it also sums the segment's range lengths (its key
 //      count) into the workspace;
 //   2. prefix-sums the counts into per-segment tile offsets;
-//   3. histograms the tiles by cost = number of 64-key tiles their rows see
-//      (under bottom-right causal the last row of the tile sees the most);
-//   4. scatters (segment, first row) pairs into cost-descending order, so
-//      the persistent forward kernel starts the longest tiles first.
+//   2. when the launch has few query tiles, splits long key ranges into
+//      chunks (split-K: up to the workspace's capacity, chunks of at least
+//      kMinSplitTiles key tiles) and prefix-sums the work entries;
+//   3. histograms the entries by cost = number of key tiles they cover
+//      (under bottom-right causal the last row of a tile sees the most);
+//   4. scatters the entries into cost-descending order, so the persistent
+//      forward kernel starts the longest work first.
 // The order inside one cost bucket depends on atomics, but each tile's
 // result does not depend on the order, so outputs are deterministic.
 #include "gvattn_internal.h"
@@ -93,16 +96,38 @@ __device__ int find_segment(const int32_t* seg_off, int nseg, int t) {
   return lo;
 }
 
-__device__ int tile_bucket(const PlanArgs& a, int s, int row0) {
+// Key count of segment s (0 for a segment the plan rejected).
+__device__ int seg_key_count(const PlanArgs& a, int s) {
+  return (a.g.kr_off != nullptr) ? a.ws.seg_keys[s] : a.g.used_k[s];
+}
+
+// Key tiles the query tile at row0 of segment s sees (under bottom-right
+// causal its last row sees the most).
+__device__ int tile_key_tiles(const PlanArgs& a, int s, int row0) {
   const int uq = a.g.used_q[s];
-  const int uk = (a.g.kr_off != nullptr) ? a.ws.seg_keys[s] : a.g.used_k[s];
+  const int uk = seg_key_count(a, s);
   int kend = uk;
   if (a.g.causal) {
     const int r_last = min(row0 + a.rows, uq) - 1;
     kend = max(0, min(uk, r_last + uk - uq + 1));
   }
-  const int ntk = (kend + kKeyTile - 1) / kKeyTile;
-  return min(ntk, kCostBuckets - 1);
+  return (kend + a.key_tile - 1) / a.key_tile;
+}
+
+// Work entry e (its segment s, first entry of s at e0): query tile
+// (e - e0) / S and key chunk (e - e0) % S of the segment's S = seg_split[s]
+// chunks; the chunk covers key tiles [kt0, kt1) of that query tile.
+__device__ int4 make_entry(const PlanArgs& a, int s, int e0, int e, int* cost) {
+  const int S = a.ws.seg_split[s];
+  const int local = e - e0;
+  const int qt = local / S, j = local - qt * S;
+  const int row0 = qt * a.rows;
+  const int nkt = tile_key_tiles(a, s, row0);
+  const int chunk = (nkt + S - 1) / S;
+  const int kt0 = min(j * chunk, nkt);
+  const int kt1 = min(kt0 + chunk, nkt);
+  *cost = min(kt1 - kt0, kCostBuckets - 1);
+  return make_int4(s, row0, kt0, (kt1 << 5) | (j << 1) | (S > 1 ? 1 : 0));
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
@@ -110,18 +135,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int tmp[kPlanThreads];
   __shared__ int hist[kCostBuckets];
   __shared__ int s_err;
+  __shared__ int s_max_split;
   const int tid = threadIdx.x;
   const int nseg = a.g.nseg;
   int32_t* seg_off = a.ws.seg_tile_off;
 
   for (int b = tid; b < kCostBuckets; b += kPlanThreads) hist[b] = 0;
-  if (tid == 0) s_err = 0;
+  if (tid == 0) {
+    s_err = 0;
+    s_max_split = 1;
+  }
   __syncthreads();
 
-  // 1-2. tile counts and their offsets.  Segments whose capacities
-  // overlap can claim more tiles than the list holds; the whole plan is
-  // then rejected (no tiles) rather than written past the workspace.
-  long long carry = 0;
+  // 1. validation and query tiles per segment (an invalid segment: none).
+  //    seg_split holds the segment's query-tile count until step 2.
+  long long n_qtiles = 0;
   for (int base = 0; base < nseg; base += kPlanThreads) {
     const int s = base + tid;
     long long cnt = 0;
@@ -129,14 +157,47 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int err = segment_error(a, s);
       if (err) atomicOr(&s_err, err);
       else cnt = (a.g.used_q[s] + a.rows - 1) / a.rows;
+      a.ws.seg_split[s] = (int32_t)cnt;
+    }
+    long long tot;
+    block_exclusive_scan<long long>(cnt, tmp64, &tot);
+    n_qtiles += tot;
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // 2. split-K decision, then entry counts and their offsets.  Segments
+  // whose capacities overlap can claim more entries than the list holds;
+  // the whole plan is then rejected (no entries) rather than written past
+  // the workspace.
+  const long long items = n_qtiles * a.n_head_chunks;
+  const bool split_on = a.ws.splits > 1 && a.g.kr_off == nullptr && items > 0 &&
+                        items < kSplitBelow;
+  const int s_aim = split_on ? (int)min((long long)a.ws.splits,
+                                        (kSplitAim + items - 1) / items) : 1;
+  const long long cap = (long long)a.max_tiles * a.ws.splits;
+  long long carry = 0;
+  for (int base = 0; base < nseg; base += kPlanThreads) {
+    const int s = base + tid;
+    long long cnt = 0;
+    if (s < nseg) {
+      const int qt = a.ws.seg_split[s];
+      int S = 1;
+      if (split_on && qt > 0) {
+        const int kt = (seg_key_count(a, s) + a.key_tile - 1) / a.key_tile;
+        S = max(1, min(s_aim, kt / kMinSplitTiles));
+      }
+      a.ws.seg_split[s] = S;
+      if (S > 1) atomicMax(&s_max_split, S);
+      cnt = (long long)qt * S;
     }
     long long tot;
     const long long excl = block_exclusive_scan<long long>(cnt, tmp64, &tot);
-    if (s < nseg) seg_off[s] = (int32_t)min(carry + excl, (long long)a.max_tiles);
+    if (s < nseg) seg_off[s] = (int32_t)min(carry + excl, cap);
     carry += tot;
   }
-  int n_tiles = (int)min(carry, (long long)a.max_tiles);
-  if (carry > a.max_tiles) {
+  int n_tiles = (int)min(carry, cap);
+  if (carry > cap) {
     n_tiles = 0;
     if (tid == 0) s_err |= GVATTN_DEVERR_OFFSETS;
   }
@@ -147,8 +208,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // 3. cost histogram
   for (int t = tid; t < n_tiles; t += kPlanThreads) {
     const int s = find_segment(seg_off, nseg, t);
-    const int row0 = (t - seg_off[s]) * a.rows;
-    atomicAdd(&hist[tile_bucket(a, s, row0)], 1);
+    int cost;
+    make_entry(a, s, seg_off[s], t, &cost);
+    atomicAdd(&hist[cost], 1);
   }
   __syncthreads();
 
@@ -166,9 +228,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // 4. scatter
   for (int t = tid; t < n_tiles; t += kPlanThreads) {
     const int s = find_segment(seg_off, nseg, t);
-    const int row0 = (t - seg_off[s]) * a.rows;
-    const int pos = atomicAdd(&hist[tile_bucket(a, s, row0)], 1);
-    a.ws.tiles[pos] = make_int2(s, row0);
+    int cost;
+    const int4 e = make_entry(a, s, seg_off[s], t, &cost);
+    const int pos = atomicAdd(&hist[cost], 1);
+    a.ws.tiles[pos] = e;
   }
   __syncthreads();
 
@@ -177,6 +240,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.ws.header->err = s_err;
     a.ws.header->key = a.key;
     a.ws.header->rows_per_tile = a.rows;
+    a.ws.header->max_split = s_max_split;
   }
 }
 

@@ -316,6 +316,21 @@ def ulysses_joint(seed: int = 6, ranks: int = 2, text_cap: int = 4096, video: in
                     note="rank-major keys; pad-slot K/V exactly zero")
 
 
+def decode_batch(seed: int = 7, batch: int = 32, new_tokens: int = 4, k_lo: int = 4096,
+                 k_hi: int = 16384, hq: int = 32, hkv: int = 8, d: int = 128,
+                 dtype: str = BF16) -> Workload:
+    """Decode-like launch (few query rows, long keys): ``batch`` segments of
+    ``new_tokens`` query rows each attend their cache of U{k_lo..k_hi} keys,
+    bottom-right causal.  Too few query tiles to fill the GPU: the plan
+    splits the key ranges (split-K)."""
+    rng = np.random.default_rng(seed)
+    uk = rng.integers(k_lo, k_hi, size=batch, endpoint=True)
+    g = make_geometry([new_tokens] * batch, uk, [new_tokens] * batch, uk, hq, hkv, d,
+                      causal=True, dtype=dtype)
+    q, k, v = fill_qkv(g, seed)
+    return Workload(f"{dtype}_decode_b{batch}x{new_tokens}_k{k_lo}_{k_hi}", seed, g, q, k, v)
+
+
 def random_ranges(rng, nseg: int, total_k: int, max_ranges: int = 4, max_len: int = 80):
     """Seeded key ranges for parity sweeps: 0..max_ranges ranges per segment,
     lengths 0..max_len (some empty), starts anywhere in [0, total_k - len];

@@ -62,14 +62,14 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    ws = lib.gvattn_fwd_workspace_size(64, 131072, 32, 8, 128, B.GVATTN_BF16)
+    ws = lib.gvattn_fwd_workspace_size(64, 131072, 32, 8, 128, 128, B.GVATTN_BF16)
     assert ws > 256 and ws % 256 == 0
     # grows with the number of query rows, never depends on device data
-    assert lib.gvattn_fwd_workspace_size(64, 2 * 131072, 32, 8, 128, B.GVATTN_BF16) > ws
-    assert lib.gvattn_fwd_workspace_size(64, 1000, 32, 7, 128, B.GVATTN_BF16) == 0  # hq % hkv
-    assert lib.gvattn_fwd_workspace_size(64, 1000, 32, 8, 96, B.GVATTN_BF16) == 0   # head dim
-    assert lib.gvattn_fwd_workspace_size(-1, 1000, 32, 8, 128, B.GVATTN_BF16) == 0
-    assert lib.gvattn_fwd_workspace_size(3, 192, 8, 2, 64, B.GVATTN_FP32) > 0
+    assert lib.gvattn_fwd_workspace_size(64, 2 * 131072, 32, 8, 128, 128, B.GVATTN_BF16) > ws
+    assert lib.gvattn_fwd_workspace_size(64, 1000, 32, 7, 128, 128, B.GVATTN_BF16) == 0  # hq % hkv
+    assert lib.gvattn_fwd_workspace_size(64, 1000, 32, 8, 96, 96, B.GVATTN_BF16) == 0   # head dim
+    assert lib.gvattn_fwd_workspace_size(-1, 1000, 32, 8, 128, 128, B.GVATTN_BF16) == 0
+    assert lib.gvattn_fwd_workspace_size(3, 192, 8, 2, 64, 64, B.GVATTN_FP32) > 0
 
 
 def _fwd(lib, fn="gvattn_fwd", **over):
@@ -83,7 +83,7 @@ def _fwd(lib, fn="gvattn_fwd", **over):
 
 @pytest.mark.parametrize("fn", ["gvattn_fwd", "gvattn_fwd_run"])
 def test_fwd_host_validation(lib, fn):
-    ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, B.GVATTN_BF16)
+    ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, 128, B.GVATTN_BF16)
     assert _fwd(lib, fn, dtype=5, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
     assert _fwd(lib, fn, d=96, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
     assert _fwd(lib, fn, dv=96, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
@@ -107,7 +107,7 @@ def test_fwd_host_validation(lib, fn):
 
 
 def test_plan_host_validation(lib):
-    ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, B.GVATTN_BF16)
+    ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, 64, B.GVATTN_BF16)  # d_v 64
     base = [B.GVATTN_BF16, FAKE, FAKE, FAKE, FAKE, 4, 1024, 1024, 8, 2, 128, 64, 1, FAKE, ok_ws,
             None]
     bad = list(base)
@@ -137,7 +137,7 @@ def _fwd_ranges(lib, **over):
 
 
 def test_fwd_ranges_host_validation(lib):
-    ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, B.GVATTN_BF16)
+    ok_ws = lib.gvattn_fwd_workspace_size(4, 1024, 8, 2, 128, 256, B.GVATTN_BF16)  # d_v 256
     assert _fwd_ranges(lib, dtype=5, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
     assert _fwd_ranges(lib, d=96, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
     assert _fwd_ranges(lib, hkv=3, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG

@@ -341,3 +341,45 @@ def test_merge_small(pdt, odt):
                   f"merge end-to-end {pdt}->{odt}", o_abs=2 * o_abs)
     say(f"[merge end-to-end {pdt}->{odt}]", st2)
     check_gap_rows(out, lse, g)
+
+
+# --- split-K (few query tiles, long keys) ----------------------------------------
+
+def max_split(ws) -> int:
+    """Most key chunks the plan split a query tile into (plan header)."""
+    return int(ws[16:20].cpu().numpy().view(np.int32)[0])
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
+@pytest.mark.parametrize("d,dv", [(128, 128), (64, 64), (256, 256), (128, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_k_decode(dtype, d, dv, causal):
+    """Decode-like launch: six segments with 0-40 used query rows and up to
+    3000 keys (one empty, one without keys).  Too few query tiles to fill
+    the GPU, so the plan splits the key ranges; every used row against the
+    oracle, a second run on the same plan is bit-identical."""
+    uq = [1, 7, 40, 0, 3, 33]
+    uk = [3000, 2500, 1200, 900, 0, 1999]
+    g = W.make_geometry([u + 5 for u in uq], [u + 7 for u in uk], uq, uk, 8, 2, d, causal,
+                        dtype=dtype, dv=dv)
+    q, k, v = W.fill_qkv(g, 600 + d + dv)
+    wl = W.Workload("decode", 600, g, q, k, v)
+    dc = DeviceCase(wl)
+    out, lse, ws = dc.fwd()
+    assert B.gvattn_read_device_error(ws) == 0
+    assert max_split(ws) > 1
+    st = compare_full(out, lse, wl, where=f"split {dtype} d{d} dv{dv} c{int(causal)}",
+                      derived=True)
+    say(f"[split-K] {dtype} d={d} dv={dv} causal={causal} max split {max_split(ws)}", st)
+    out2, lse2, _ = dc.fwd(fn=B.gvattn_fwd_run, workspace=ws)
+    t = torch()
+    assert t.equal(out.view(t.int16), out2.view(t.int16))
+    assert t.equal(lse.view(t.int32), lse2.view(t.int32))
+
+
+def test_no_split_when_the_gpu_is_full():
+    """Enough query tiles: the plan does not split."""
+    wl = W.random_small(610, 40, 256, 300, 32, 8, 128, True, W.BF16)
+    out, lse, ws = DeviceCase(wl).fwd()
+    assert max_split(ws) == 1
+    compare_full(out, lse, wl, where="no split", derived=True)
