@@ -7,6 +7,7 @@ leg may import this package.  The HIP path never does.
 from .gvattn_oracle import (  # noqa: F401
     SCORE_BUDGET_BYTES,
     attention_flops,
+    attention_bwd,
     attention_fwd,
     attention_fwd_ranges,
     bits_equal,

@@ -19,6 +19,9 @@ What it computes (the sources are the pages' own statements of the method):
 * cosmos-framework PR #312, "Problem and behavior": GQA folding (several query
   heads share one KV head) and an FP32 LSE merge of the partial results of
   visibility partitions.
+* The gradients (``attention_bwd``): the pages' path is forward-only (PR
+  #302 makes the backward raise); the backward here is the calculus of the
+  forward above, written out.
 * TensorRT-LLM issue #18687, "Suggested fix" item 1: after the Ulysses
   all-to-all the keys arrive rank-major, so a sample's valid keys are several
   runs of rows rather than one prefix.  ``attention_fwd_ranges`` takes each
@@ -221,6 +224,58 @@ def attention_fwd_ranges(q, k, v, cu_q, used_q, kr_off, kr_start, kr_len, scale,
     return out, lse
 
 
+def attention_bwd(q, k, v, do, cu_q, cu_k, used_q, used_k, scale, causal,
+                  dq_init=None, dk_init=None, dv_init=None):
+    """Gradients of the segmented forward, from its definition, in float64.
+
+    For every segment and query head h (KV head g = h // (Hq/Hkv)), with
+    S = scale * Q K^T over the used rows and keys (masked entries -inf),
+    P = softmax(S) row by row (a row with no visible key has P = 0) and
+    O = P V:  dV_g += P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dP * P)),
+    dQ = scale * dS K,  dK_g += scale * dS^T Q.  The heads of a KV group add
+    into one dK / dV.  Rows outside the used prefixes keep the initial
+    values (zeros when not given); used keys that no row sees get 0.
+    The pages' path is forward-only; this is the plain calculus of the
+    forward they define."""
+    tq, hq, d = q.shape
+    tk, hkv, dv = v.shape
+    grp = hq // hkv
+    dq = np.zeros((tq, hq, d)) if dq_init is None else np.array(dq_init, np.float64, copy=True)
+    dk = np.zeros((tk, hkv, d)) if dk_init is None else np.array(dk_init, np.float64, copy=True)
+    dvo = np.zeros((tk, hkv, dv)) if dv_init is None else np.array(dv_init, np.float64, copy=True)
+    for s in range(len(used_q)):
+        q0, k0 = int(cu_q[s]), int(cu_k[s])
+        uq, uk = int(used_q[s]), int(used_k[s])
+        if uq > 0:
+            dq[q0:q0 + uq] = 0.0
+        if uk > 0:
+            dk[k0:k0 + uk] = 0.0
+            dvo[k0:k0 + uk] = 0.0
+        if uq == 0 or uk == 0:
+            continue
+        lim = visible_limit(np.arange(uq), uq, uk, causal)
+        vis = np.arange(uk)[None, :] < lim[:, None]                  # [uq, uk]
+        live = lim > 0
+        for h in range(hq):
+            g = h // grp
+            qs = np.asarray(q[q0:q0 + uq, h], np.float64)
+            ks = np.asarray(k[k0:k0 + uk, g], np.float64)
+            vs = np.asarray(v[k0:k0 + uk, g], np.float64)
+            dos = np.asarray(do[q0:q0 + uq, h], np.float64)
+            sc = float(scale) * (qs @ ks.T)
+            sc = np.where(vis, sc, -np.inf)
+            p = np.zeros_like(sc)
+            m = sc[live].max(axis=1, keepdims=True)
+            e = np.exp(sc[live] - m)
+            p[live] = e / e.sum(axis=1, keepdims=True)
+            dvo[k0:k0 + uk, g] += p.T @ dos
+            dp = dos @ vs.T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dq[q0:q0 + uq, h] = float(scale) * (ds @ ks)
+            dk[k0:k0 + uk, g] += float(scale) * (ds.T @ qs)
+    return dq, dk, dvo
+
+
 class _NullCtx:
     def __enter__(self):
         return self
@@ -289,6 +344,6 @@ def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
 
 
 __all__ = [
-    "attention_fwd", "attention_fwd_ranges", "segment_key_rows", "lse_merge", "segment_head_rows", "visible_limit",
+    "attention_fwd", "attention_fwd_ranges", "attention_bwd", "segment_key_rows", "lse_merge", "segment_head_rows", "visible_limit",
     "attention_flops", "host_cores", "bits_equal", "SCORE_BUDGET_BYTES",
 ]

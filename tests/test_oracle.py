@@ -564,3 +564,100 @@ def test_ranges_single_prefix_and_order():
             fin = np.isfinite(l4)
             assert np.array_equal(np.isneginf(l3), np.isneginf(l4))
             assert np.max(np.abs(o3 - o4)) < 1e-12 and np.max(np.abs(l3[fin] - l4[fin])) < 1e-12
+
+
+# --- gradients (the backward of the forward above) ------------------------------
+
+def _bwd_case(seed, caps_q, caps_k, uq, uk, hq, hkv, d, dv, causal):
+    rng = np.random.default_rng(seed)
+    g = W.make_geometry(caps_q, caps_k, uq, uk, hq, hkv, d, causal, dtype=W.FP32, dv=dv)
+    q = rng.standard_normal((g.total_q, hq, d))
+    k = rng.standard_normal((g.total_k, hkv, d))
+    v = rng.standard_normal((g.total_k, hkv, dv))
+    do = rng.standard_normal((g.total_q, hq, dv))
+    return g, q, k, v, do
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_autograd_per_segment(causal):
+    """Per segment, torch autograd in float64 through SDPA with an explicit
+    key mask (bottom-right causal built by hand) gives the same dQ, dK, dV."""
+    g, q, k, v, do = _bwd_case(70 + causal, [9, 6, 12], [11, 5, 7], [9, 0, 10], [11, 4, 3],
+                               6, 2, 8, 5, causal)
+    scale = 0.31
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, g.cu_q, g.cu_k, g.used_q, g.used_k, scale,
+                                      causal)
+    for s in range(g.nseg):
+        q0, k0, uq, uk = int(g.cu_q[s]), int(g.cu_k[s]), int(g.used_q[s]), int(g.used_k[s])
+        if uq == 0 or uk == 0:
+            continue
+        tq = torch.tensor(q[q0:q0 + uq], requires_grad=True)
+        tk = torch.tensor(k[k0:k0 + uk], requires_grad=True)
+        tv = torch.tensor(v[k0:k0 + uk], requires_grad=True)
+        i = torch.arange(uq)[:, None]
+        j = torch.arange(uk)[None, :]
+        mask = (j <= i + uk - uq) if causal else torch.ones(uq, uk, dtype=torch.bool)
+        live = mask.any(dim=1)
+        o = F.scaled_dot_product_attention(tq.permute(1, 0, 2)[None][:, :, live],
+                                           tk.permute(1, 0, 2)[None], tv.permute(1, 0, 2)[None],
+                                           attn_mask=mask[live][None, None], scale=scale,
+                                           enable_gqa=True)
+        o.backward(torch.from_numpy(do[q0:q0 + uq]).permute(1, 0, 2)[None][:, :, live])
+        want_q = np.zeros((uq, 6, 8))
+        want_q[live.numpy()] = tq.grad.numpy()[live.numpy()]
+        assert np.max(np.abs(dq[q0:q0 + uq] - want_q)) < 1e-10
+        assert np.max(np.abs(dk[k0:k0 + uk] - tk.grad.numpy())) < 1e-10
+        assert np.max(np.abs(dv[k0:k0 + uk] - tv.grad.numpy())) < 1e-10
+
+
+def test_bwd_finite_differences():
+    """Central differences of L = sum(O * W) against the analytic gradient,
+    on a tiny two-segment causal GQA case (independent of torch)."""
+    g, q, k, v, W_ = _bwd_case(73, [4, 3], [5, 4], [4, 3], [5, 2], 4, 2, 3, 2, True)
+    scale = 0.7
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention_fwd(q_, k_, v_, g.cu_q, g.cu_k, g.used_q, g.used_k, scale, True,
+                                    workers=1)
+        return float(np.sum(o * W_))
+
+    dq, dk, dv = oracle.attention_bwd(q, k, v, W_, g.cu_q, g.cu_k, g.used_q, g.used_k, scale,
+                                      True)
+    eps = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            up = loss(q, k, v)
+            arr[idx] = old - eps
+            dn = loss(q, k, v)
+            arr[idx] = old
+            assert abs((up - dn) / (2 * eps) - grad[idx]) < 1e-7, idx
+
+
+def test_bwd_gqa_sum_gaps_and_dead_rows():
+    """dK / dV of a KV head are the sums over its query heads (the repeated-
+    head problem's gradients added up); gap rows keep their initial values;
+    rows and keys that take part in nothing get exact zeros."""
+    g, q, k, v, do = _bwd_case(74, [7, 5], [9, 6], [6, 4], [8, 2], 6, 2, 4, 4, True)
+    scale = 0.5
+    sent = 7.0
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, g.cu_q, g.cu_k, g.used_q, g.used_k, scale,
+                                      True, np.full((g.total_q, 6, 4), sent),
+                                      np.full((g.total_k, 2, 4), sent),
+                                      np.full((g.total_k, 2, 4), sent))
+    # repeated heads: KV head h // 3 copied per query head, MHA gradients summed
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    dq2, dk2, dv2 = oracle.attention_bwd(q, kr, vr, do, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                                         scale, True)
+    used_k = np.concatenate([np.arange(g.cu_k[s], g.cu_k[s] + g.used_k[s]) for s in range(2)])
+    assert np.max(np.abs(dk[used_k] - dk2[used_k].reshape(-1, 2, 3, 4).sum(2))) < 1e-12
+    assert np.max(np.abs(dv[used_k] - dv2[used_k].reshape(-1, 2, 3, 4).sum(2))) < 1e-12
+    used_q = np.concatenate([np.arange(g.cu_q[s], g.cu_q[s] + g.used_q[s]) for s in range(2)])
+    assert np.max(np.abs(dq[used_q] - dq2[used_q])) < 1e-12
+    gap_q = np.setdiff1d(np.arange(g.total_q), used_q)
+    gap_k = np.setdiff1d(np.arange(g.total_k), used_k)
+    assert np.all(dq[gap_q] == sent) and np.all(dk[gap_k] == sent) and np.all(dv[gap_k] == sent)
+    # segment 1: 4 rows, 2 keys, bottom-right causal: rows 0 and 1 see nothing
+    r0 = int(g.cu_q[1])
+    assert np.all(dq[r0:r0 + 2] == 0.0)
