@@ -106,6 +106,8 @@ def main():
                     help="config 4: both partitions as key ranges of one launch")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the backward (gvattn_bwd) record")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the "
@@ -263,6 +265,36 @@ def main():
                      "frac_of_hbm_peak": round(mbytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] LSE merge alone: {merge_ms:.4f} ms, {merge_rec['GB_per_s']} GB/s")
 
+    bwd_rec = None
+    if (not args.no_bwd and wl.key_ranges is None and args.config != 4 and g.d <= 128
+            and g.dv <= 128):
+        # gradients of the same step: dO seeded, O / LSE from the forward
+        # above; FLOPs counted as the five products of the calculus (S, dP,
+        # dV, dQ, dK), although the kernels recompute S and dP once more
+        dout = up(W.normal_tensor(wl.seed, 7, (g.total_q, g.hq, g.dv), 1.0, args.dtype)).to(tdt)
+        dq, dk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        (cu_k0, used_k0), (o0, l0), _ = launches[0], parts[0], wss[0]
+        step()
+        bws = gv.gvattn_bwd(q, k, v, o0, dout, l0, cu_q, cu_k0, used_q, used_k0, dq, dk, dvv,
+                            float(g.scale), g.causal)
+        for _ in range(max(1, args.warmup)):
+            gv.gvattn_bwd(q, k, v, o0, dout, l0, cu_q, cu_k0, used_q, used_k0, dq, dk, dvv,
+                          float(g.scale), g.causal, workspace=bws)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(args.steps):
+            gv.gvattn_bwd(q, k, v, o0, dout, l0, cu_q, cu_k0, used_q, used_k0, dq, dk, dvv,
+                          float(g.scale), g.causal, workspace=bws)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / args.steps
+        bflops = flops // (2 * g.d + 2 * g.dv) * (6 * g.d + 4 * g.dv)
+        btf = bflops / (bwd_ms * 1e-3) / 1e12
+        bwd_rec = {"ms": round(bwd_ms, 5), "flop": bflops, "TFLOP_per_s": round(btf, 3),
+                   "frac_of_peak": round(btf / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] backward: {bwd_ms:.4f} ms, {btf:.1f} TFLOP/s")
+        del dout, dq, dk, dvv, bws
+
     tflops = flops / (ms * 1e-3) / 1e12
     achieved = kern_flops / (kern_ms * 1e-3) / 1e12
     traffic_rec = recorded_traffic() if (args.config == 3 and args.dtype == "bf16") else None
@@ -296,6 +328,8 @@ def main():
     }
     if merge_rec is not None:
         res["merge"] = merge_rec
+    if bwd_rec is not None:
+        res["backward"] = bwd_rec
     if not args.no_cpu_baseline and args.config == 3 and args.dtype == "bf16":
         log("[bench] timing the oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_seconds)

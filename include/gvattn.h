@@ -1,6 +1,6 @@
 /*
- * gvattn -- segmented ("gapped") variable-length attention forward and LSE
- * merge for AMD Instinct MI355X (gfx950).  Plain C ABI: pointers and sizes
+ * gvattn -- segmented ("gapped") variable-length attention forward, LSE
+ * merge and gradients for AMD Instinct MI355X (gfx950).  Plain C ABI: pointers and sizes
  * only, no C++ or framework types.
  *
  * The operation (the sources are the pages this library implements):
@@ -238,6 +238,59 @@ int gvattn_lse_merge(int32_t nparts, const void* const* part_out,
 
 /* Static text for a gvattn_status value. */
 const char* gvattn_status_string(int status);
+
+/*
+ * Bytes of device workspace gvattn_bwd needs: two plans (query tiles for
+ * dQ, 128-key tiles for dK / dV) and 8 bytes of per-row statistics per
+ * (query head, query row).  Depends only on host-known sizes.  Returns 0
+ * for invalid or unsupported arguments.
+ */
+size_t gvattn_bwd_workspace_size(int32_t nseg, int32_t total_q, int32_t total_k,
+                                 int32_t hq, int32_t hkv, int32_t d, int32_t d_v,
+                                 int32_t dtype);
+
+/*
+ * Gradients of gvattn_fwd with respect to Q, K and V.  The pages' path is
+ * forward-only (PR #302, review: its backward raises); this is the plain
+ * calculus of the forward they define (PR #302, "What"; PR #312, "Problem
+ * and behavior").  Per segment and query head h (KV head g = h / (hq/hkv)),
+ * with P = exp(softmax_scale * Q K^T - LSE) over the used rows and the keys
+ * each row sees, and D = rowsum(dO * O):
+ *   dV_g = sum_h P^T dO,   dS = P * (dO V^T - D),
+ *   dQ   = softmax_scale * dS K,   dK_g = softmax_scale * sum_h dS^T Q.
+ *
+ *   dtype            GVATTN_BF16 or GVATTN_FP16 (fp32 accumulation; P and
+ *                    dS rounded to nearest even for the matrix cores).
+ *                    GVATTN_FP32 returns GVATTN_ERR_UNSUPPORTED.
+ *   q, k, v          the forward's inputs (layouts above).
+ *   out, lse         the forward's outputs for the same inputs: O
+ *                    [total_q, hq, d_v], LSE fp32 [hq, total_q].  Only
+ *                    used rows are read.
+ *   dout             dL/dO, [total_q, hq, d_v], dtype.  Only used rows are
+ *                    read.
+ *   cu_seqlens_*, seqused_*, nseg, total_*, hq, hkv, softmax_scale, causal
+ *                    as in gvattn_fwd (the key-prefix form).
+ *   d, d_v           64 or 128 each (others: GVATTN_ERR_UNSUPPORTED).
+ *   dq               [total_q, hq, d]: written for used rows (0 for a row
+ *                    that sees no key); other rows are left untouched.
+ *   dk, dv           [total_k, hkv, d] and [total_k, hkv, d_v]: written for
+ *                    the used keys of every segment (0 for a key no row
+ *                    sees); other rows are left untouched.
+ *                    dq, dk and dv must not overlap each other or any input.
+ *   workspace        device, GVATTN_WORKSPACE_ALIGN-aligned, at least
+ *                    gvattn_bwd_workspace_size(...) bytes.
+ * Device-data errors are reported as for gvattn_fwd (the affected segment
+ * is skipped; gvattn_read_device_error on this workspace).
+ */
+int gvattn_bwd(int32_t dtype, const void* q, const void* k, const void* v,
+               const void* out, const void* dout, const float* lse,
+               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+               const int32_t* seqused_q, const int32_t* seqused_k,
+               int32_t nseg, int32_t total_q, int32_t total_k,
+               int32_t hq, int32_t hkv, int32_t d, int32_t d_v,
+               float softmax_scale, int32_t causal,
+               void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * Debugging aid: waits for `hip_stream`, then copies the device error word

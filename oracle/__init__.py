@@ -8,6 +8,7 @@ from .gvattn_oracle import (  # noqa: F401
     SCORE_BUDGET_BYTES,
     attention_flops,
     attention_bwd,
+    attention_bwd_magnitudes,
     attention_fwd,
     attention_fwd_ranges,
     bits_equal,

@@ -276,6 +276,55 @@ def attention_bwd(q, k, v, do, cu_q, cu_k, used_q, used_k, scale, causal,
     return dq, dk, dvo
 
 
+def attention_bwd_magnitudes(q, k, v, do, cu_q, cu_k, used_q, used_k, scale, causal):
+    """Absolute-value sums that bound the rounding error of a backward that
+    rounds P, dS and O to a 16-bit type (used by the tests to state their
+    tolerance; not a result of the method).  With P and dS as in
+    ``attention_bwd``, O = P V and Dabs_i = sum_e |dO_ie| |O_ie|:
+
+        A_dv[j] = sum_h sum_i P_ij |dO_i|
+        A_dq[i] = scale * sum_j (|dS_ij| + P_ij * Dabs_i) |K_j|
+        A_dk[j] = scale * sum_h sum_i (|dS_ij| + P_ij * Dabs_i) |Q_i|
+
+    Rounding P (for dV), dS (for dQ, dK) and O (in D = rowsum(dO * O)) with
+    unit roundoff u, and accumulating in FP32, leaves each gradient within
+    about u * (|exact| + A) of the exact one.  Returns (A_dq, A_dk, A_dv)
+    with the shapes of the gradients; zero outside the used rows."""
+    tq, hq, d = q.shape
+    tk, hkv, dv = v.shape
+    grp = hq // hkv
+    a_dq = np.zeros((tq, hq, d))
+    a_dk = np.zeros((tk, hkv, d))
+    a_dv = np.zeros((tk, hkv, dv))
+    for s in range(len(used_q)):
+        q0, k0 = int(cu_q[s]), int(cu_k[s])
+        uq, uk = int(used_q[s]), int(used_k[s])
+        if uq == 0 or uk == 0:
+            continue
+        lim = visible_limit(np.arange(uq), uq, uk, causal)
+        vis = np.arange(uk)[None, :] < lim[:, None]
+        live = lim > 0
+        for h in range(hq):
+            g = h // grp
+            qs = np.asarray(q[q0:q0 + uq, h], np.float64)
+            ks = np.asarray(k[k0:k0 + uk, g], np.float64)
+            vs = np.asarray(v[k0:k0 + uk, g], np.float64)
+            dos = np.asarray(do[q0:q0 + uq, h], np.float64)
+            sc = np.where(vis, float(scale) * (qs @ ks.T), -np.inf)
+            p = np.zeros_like(sc)
+            m = sc[live].max(axis=1, keepdims=True)
+            e = np.exp(sc[live] - m)
+            p[live] = e / e.sum(axis=1, keepdims=True)
+            dp = dos @ vs.T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dabs = (np.abs(dos) * np.abs(p @ vs)).sum(axis=1, keepdims=True)
+            w = np.abs(ds) + p * dabs
+            a_dv[k0:k0 + uk, g] += p.T @ np.abs(dos)
+            a_dq[q0:q0 + uq, h] = float(scale) * (w @ np.abs(ks))
+            a_dk[k0:k0 + uk, g] += float(scale) * (w.T @ np.abs(qs))
+    return a_dq, a_dk, a_dv
+
+
 class _NullCtx:
     def __enter__(self):
         return self

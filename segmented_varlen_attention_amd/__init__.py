@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     GVATTN_FP16,
     GVATTN_FP32,
     alloc_workspace,
+    gvattn_bwd,
+    gvattn_bwd_workspace_size,
     gvattn_fwd,
     gvattn_fwd_plan,
     gvattn_fwd_ranges,

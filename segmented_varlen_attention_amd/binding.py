@@ -54,6 +54,10 @@ SIGNATURES = {
                                          _vp, _vp, _vp, _sz, _vp]),
     "gvattn_lse_merge": (ctypes.c_int, [_i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32,
                                         _i32, _vp, _vp, _vp, _vp]),
+    "gvattn_bwd_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "gvattn_bwd": (ctypes.c_int, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp,
+                                  _vp, _sz, _vp]),
     "gvattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gvattn_read_device_error": (ctypes.c_int, [_vp, _vp, ctypes.POINTER(_i32)]),
     "gvattn_version": (ctypes.c_int, []),
@@ -225,6 +229,40 @@ def gvattn_fwd_ranges(q, k, v, cu_seqlens_q, seqused_q, kr_off, kr_start, kr_len
         d, dv, float(softmax_scale), int(bool(causal)), out.data_ptr(), lse.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream_ptr(stream))
     _check(rc, "gvattn_fwd_ranges")
+    return workspace
+
+
+def gvattn_bwd_workspace_size(nseg: int, total_q: int, total_k: int, hq: int, hkv: int, d: int,
+                              d_v: int, dtype: int) -> int:
+    return int(load_library().gvattn_bwd_workspace_size(nseg, total_q, total_k, hq, hkv, d, d_v,
+                                                        dtype))
+
+
+def gvattn_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k,
+               dq, dk, dv, softmax_scale, causal=False, workspace=None, stream=None):
+    """Gradients of gvattn_fwd: writes dq, dk, dv for the used rows and keys
+    (other rows untouched).  `out` / `lse` are the forward's outputs for the
+    same inputs, `dout` the gradient of `out`.  Returns the workspace."""
+    torch = _torch()
+    nseg, total_q, total_k, hq, hkv, d, d_v = _fwd_common(
+        q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, lse)
+    for name, t, ref in (("dout", dout, out), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+        _need(t.dtype == ref.dtype and tuple(t.shape) == tuple(ref.shape),
+              f"{name} must be {ref.dtype} {tuple(ref.shape)}, got {t.dtype} {tuple(t.shape)}")
+    dt = _dtype_code(q)
+    if workspace is None:
+        n = gvattn_bwd_workspace_size(nseg, total_q, total_k, hq, hkv, d, d_v, dt)
+        if n == 0:
+            raise ValueError("gvattn_bwd: unsupported dtype or head dim, or invalid geometry")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    rc = load_library().gvattn_bwd(
+        dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), seqused_q.data_ptr(),
+        seqused_k.data_ptr(), nseg, total_q, total_k, hq, hkv, d, d_v, float(softmax_scale),
+        int(bool(causal)), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream_ptr(stream))
+    _check(rc, "gvattn_bwd")
     return workspace
 
 

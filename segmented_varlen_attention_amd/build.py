@@ -28,6 +28,7 @@ SOURCES = [
     "gvattn_fwd_mfma.hip",
     "gvattn_fwd_fp32.hip",
     "gvattn_merge.hip",
+    "gvattn_bwd.hip",
 ]
 
 # Packed FP32 VALU ops are kept out of the generated code; the host pass

@@ -126,6 +126,7 @@ int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
   PlanArgs a;
   a.g = g;
   a.ws = view_workspace(ws, L);
+  a.mode = 0;
   a.rows = t.rows;
   a.max_tiles = (int32_t)L.max_tiles;
   a.key_tile = key_tile(g.d, g.dv);
@@ -173,6 +174,81 @@ int check_fwd_args(int32_t dtype, const void* q, const void* k, const void* v,
   if (!q || !k || !v || !cu_q || !cu_k || !used_q || !used_k || !out || !lse)
     return GVATTN_ERR_INVALID_ARG;
   return check_workspace(ws, ws_bytes, layout_of(dtype, nseg, total_q, hq, hkv, d, dv));
+}
+
+// ---- backward --------------------------------------------------------------
+
+constexpr int kPlanBwdQ = 1 << 20, kPlanBwdK = 2 << 20;  // plan-key flags
+
+bool bwd_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+int check_bwd_sizes(int32_t dtype, int32_t nseg, int32_t total_q, int32_t total_k, int32_t hq,
+                    int32_t hkv, int32_t d, int32_t dv, int32_t causal) {
+  const int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, dv, causal);
+  if (rc != GVATTN_OK) return rc;
+  if (dtype == GVATTN_FP32 || !bwd_dim_ok(d) || !bwd_dim_ok(dv)) return GVATTN_ERR_UNSUPPORTED;
+  return GVATTN_OK;
+}
+
+BwdLayout bwd_layout_of(int32_t dtype, int32_t nseg, int32_t total_q, int32_t total_k,
+                        int32_t hq, int32_t hkv, int32_t d, int32_t dv) {
+  return bwd_layout(nseg, total_q, total_k, hq, dv, choose_shape(dtype, hq, hkv, d), dtype);
+}
+
+int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const void* v,
+           const void* out, const void* dout, const float* lse, float scale, void* dq,
+           void* dk, void* dv, void* ws, hipStream_t stream) {
+  const TileShape t = choose_shape(dtype, g.hq, g.hkv, g.d);
+  const BwdLayout L = bwd_layout_of(dtype, g.nseg, g.total_q, g.total_k, g.hq, g.hkv, g.d, g.dv);
+  char* base = static_cast<char*>(ws);
+  const int dmax = g.d > g.dv ? g.d : g.dv;
+  const int shape_flags = (g.d << 1) | (g.dv << 10);
+
+  PlanArgs pq;
+  pq.g = g;
+  pq.ws = view_workspace(base, L.q);
+  pq.mode = 0;
+  pq.rows = t.rows;
+  pq.max_tiles = (int32_t)L.q.max_tiles;
+  pq.key_tile = 32;
+  pq.n_head_chunks = g.hq / t.gf;
+  pq.key = plan_key(t.rows, g.causal, g.nseg, shape_flags | kPlanBwdQ);
+  pq.q_row_bytes = (int64_t)g.hq * dmax * esize(dtype);
+  pq.k_row_bytes = (int64_t)g.hkv * dmax * esize(dtype);
+  PlanArgs pk = pq;
+  pk.ws = view_workspace(base + L.kplan, L.k);
+  pk.mode = 1;
+  pk.rows = kBwdKeyRows;
+  pk.max_tiles = (int32_t)L.k.max_tiles;
+  pk.n_head_chunks = g.hkv;
+  pk.key = plan_key(kBwdKeyRows, g.causal, g.nseg, shape_flags | kPlanBwdK);
+  if (launch_plan(pq, stream) != hipSuccess) return GVATTN_ERR_HIP;
+  if (launch_plan(pk, stream) != hipSuccess) return GVATTN_ERR_HIP;
+
+  BwdArgs b;
+  b.g = g;
+  b.qws = pq.ws;
+  b.kws = pk.ws;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.o = out;
+  b.dout = dout;
+  b.lse = lse;
+  b.stats = reinterpret_cast<float*>(base + L.stats);
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.scale = scale;
+  b.scale_log2 = scale * kLog2e;
+  b.qkey = pq.key;
+  b.kkey = pk.key;
+  b.n_head_chunks = pq.n_head_chunks;
+  b.n_cu = 0;
+  bool ok = false;
+  const hipError_t e = launch_bwd(b, dtype, t, stream, &ok);
+  if (!ok) return GVATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
 }
 
 }  // namespace
@@ -307,6 +383,34 @@ int gvattn_lse_merge(int32_t nparts, const void* const* part_out, const float* c
   hipError_t e = launch_merge(a, part_dtype, out_dtype, static_cast<hipStream_t>(hip_stream), &ok);
   if (!ok) return GVATTN_ERR_UNSUPPORTED;
   return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
+}
+
+size_t gvattn_bwd_workspace_size(int32_t nseg, int32_t total_q, int32_t total_k, int32_t hq,
+                                 int32_t hkv, int32_t d, int32_t d_v, int32_t dtype) {
+  if (check_bwd_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, d_v, 0) != GVATTN_OK) return 0;
+  return bwd_layout_of(dtype, nseg, total_q, total_k, hq, hkv, d, d_v).bytes;
+}
+
+int gvattn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* out,
+               const void* dout, const float* lse, const int32_t* cu_q, const int32_t* cu_k,
+               const int32_t* used_q, const int32_t* used_k, int32_t nseg, int32_t total_q,
+               int32_t total_k, int32_t hq, int32_t hkv, int32_t d, int32_t d_v,
+               float softmax_scale, int32_t causal, void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes_, void* hip_stream) {
+  int rc = check_bwd_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
+  if (rc != GVATTN_OK) return rc;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return GVATTN_ERR_INVALID_ARG;
+  if (nseg == 0) return GVATTN_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !cu_q || !cu_k || !used_q || !used_k || !dq ||
+      !dk || !dv)
+    return GVATTN_ERR_INVALID_ARG;
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % GVATTN_WORKSPACE_ALIGN != 0 ||
+      workspace_bytes_ < bwd_layout_of(dtype, nseg, total_q, total_k, hq, hkv, d, d_v).bytes)
+    return GVATTN_ERR_WORKSPACE;
+  const Geometry g =
+      make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
+  return do_bwd(dtype, g, q, k, v, out, dout, lse, softmax_scale, dq, dk, dv, workspace,
+                static_cast<hipStream_t>(hip_stream));
 }
 
 const char* gvattn_status_string(int status) {

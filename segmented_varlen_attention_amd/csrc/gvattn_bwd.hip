@@ -1,0 +1,626 @@
+// BF16 / FP16 gradients of the segmented varlen attention forward on gfx950
+// matrix cores.
+//
+// The pages' path is forward-only (cosmos-framework PR #302, review: the
+// backward raises).  These kernels compute the plain calculus of the
+// forward they define (PR #302, "What": used prefixes, untouched gap rows;
+// PR #312, "Problem and behavior": GQA folding, FP32 LSE).  With
+// P = exp(scale * Q K^T - LSE) taken from the forward's LSE:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
+//   dQ = scale * dS K,  dK = scale * dS^T Q,
+// the query heads of a KV group adding into one dK / dV.
+//
+// Two kernels, no atomics, deterministic:
+//   * dQ: one work item = (query tile, chunk of GF query heads of one KV
+//     group), the forward's plan and static schedule.  A wave owns 32 query
+//     rows of one head with Q and dO in registers; K / V tiles of 32 keys
+//     move HBM -> LDS by buffer_load ... lds, double-buffered.  S^T = K Q^T
+//     and dP^T = V dO^T on the matrix cores leave one query row per lane
+//     column, so dS^T is formed in registers and dQ^T += K^T dS^T takes it
+//     as the B operand, K^T read transposed (ds_read_b64_tr_b16) from the
+//     row-major K tile.  The kernel also forms D from O and dO and writes
+//     (LSE * log2 e, D) per (head, row) for the second kernel.
+//   * dK / dV: one work item = (128 keys of one segment, KV head) from a
+//     key-tile plan.  Each of 4 waves owns 32 keys with K and V in
+//     registers; the group's query heads and the query tiles that see those
+//     keys stream through LDS.  S = Q K^T and dP = dO V^T leave one key per
+//     lane column, so dV^T += dO^T P and dK^T += Q^T dS take P and dS
+//     straight from the registers; Q^T and dO^T are read transposed from the
+//     row-major tiles.
+// Offsets that must be bounds-checked go in the per-lane offset operand of
+// the buffer instructions: loads past a segment's used rows or keys return
+// zero and stores there are dropped, so gap rows of dQ, dK and dV are never
+// written.  Rows past the used length and invisible keys are also masked
+// explicitly, so no value read from outside the used rows can reach a sum.
+#include <math.h>
+
+#include "gvattn_internal.h"
+#include "gvattn_mfma.h"
+
+namespace gvattn {
+namespace {
+
+using namespace dev;
+using namespace mfma;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D, int DV>
+struct BwdCfg {
+  static constexpr int CHK = D / 8;    // 16-byte chunks per Q / K row
+  static constexpr int CHV = DV / 8;   // 16-byte chunks per V / O / dO row
+  static constexpr int KK = D / 16;    // MFMA k-steps over d
+  static constexpr int KV = DV / 16;   // MFMA k-steps over d_v
+  static constexpr int DBK = D / 32;   // 32-wide blocks of d
+  static constexpr int DBV = DV / 32;  // 32-wide blocks of d_v
+  static constexpr int KP = D + 8;     // staging row pitches (elements)
+  static constexpr int VP = DV + 8;
+};
+
+// Static persistent schedule (the forward's): item w lives in queue w % 8
+// at position w / 8, so with 8 head chunks or KV heads one XCD's L2 serves
+// one KV head; the workgroups of a queue take its items in rounds, forward
+// in even rounds and backward in odd ones (the plan sorts items by
+// decreasing cost), and the wave priority rotates so that workgroups
+// dispatched in later slots of a compute unit are not starved.
+struct Schedule {
+  int q, qi, n_q, n_slots, slot;
+  __device__ __forceinline__ explicit Schedule(int n_cu) {
+    q = blockIdx.x & 7;
+    qi = blockIdx.x >> 3;
+    n_q = ((int)gridDim.x - q + 7) >> 3;
+    n_slots = min(4, ((int)gridDim.x + n_cu - 1) / n_cu);
+    slot = (int)blockIdx.x / n_cu;
+  }
+  __device__ __forceinline__ int item(int r) const {
+    const int j = r * n_q + ((r & 1) ? n_q - 1 - qi : qi);
+    return j * 8 + q;
+  }
+  __device__ __forceinline__ void priority(int r) const {
+    switch ((r + slot) % n_slots) {
+      case 0: __builtin_amdgcn_s_setprio(0); break;
+      case 1: __builtin_amdgcn_s_setprio(1); break;
+      case 2: __builtin_amdgcn_s_setprio(2); break;
+      default: __builtin_amdgcn_s_setprio(3); break;
+    }
+  }
+};
+
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, voff, 0, 0, 0);
+}
+
+// 32 x 32 block of the A operand transposed: lane (r32, hh) receives
+// column `col0 + r32` of rows {16 * a2 + 8 * (j / 4) + 4 * hh + j % 4}, j < 8,
+// of a row-major tile with `pitch` bytes per row and swizzle swz_k<W>.
+template <int W, typename v8>
+__device__ __forceinline__ v8 read_a_transposed(const char* tile, int a2, int col0, int trow,
+                                                int tcol) {
+  const int dcol = col0 + tcol;
+  const int ch = dcol >> 3, within = (dcol & 7) * 2;
+  const int r_lo = a2 * 16 + trow, r_hi = r_lo + 8;
+  const i16x4 lo = read_tr(tile + r_lo * (W * 2) + ((ch ^ swz_k<W>(r_lo)) << 4) + within);
+  const i16x4 hi = read_tr(tile + r_hi * (W * 2) + ((ch ^ swz_k<W>(r_hi)) << 4) + within);
+  return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row r32, k-step kk of a row-major tile with W elements per row, swizzle
+// swz_k<W>: the A operand of a product whose k index runs over the row.
+template <int W, typename v8>
+__device__ __forceinline__ v8 read_a_rows(const char* tile, int r32, int hh, int kk) {
+  return *reinterpret_cast<const v8*>(tile + r32 * (W * 2) + (((2 * kk + hh) ^ swz_k<W>(r32)) << 4));
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and the per-row statistics of the dK / dV kernel)
+// ---------------------------------------------------------------------------
+template <typename T, int D, int DV, int GF, int RB>
+__global__ __launch_bounds__(64 * GF * RB, 2) void bwd_dq_kernel(BwdArgs a) {
+  using C = BwdCfg<D, DV>;
+  using E = Elem<T>;
+  using v8 = typename E::v8;
+  using v4 = typename E::v4;
+  constexpr int NW = GF * RB;
+  constexpr int K_TILE = 32 * D * 2, V_TILE = 32 * DV * 2;
+  constexpr int STAGE = K_TILE + V_TILE;
+  constexpr int DMA_K = K_TILE / 1024, DMA_V = V_TILE / 1024;
+  constexpr int NDMA_K = (DMA_K + NW - 1) / NW, NDMA_V = (DMA_V + NW - 1) / NW;
+  constexpr int S_BYTES = NW * 32 * C::KP * 2;
+  constexpr int LDS_BYTES = (2 * STAGE > S_BYTES) ? 2 * STAGE : S_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+
+  const PlanHeader* hdr = a.qws.header;
+  if (hdr->key != a.qkey) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&a.qws.header->err, GVATTN_DEVERR_PLAN);
+    return;
+  }
+  const int n_hc = a.n_head_chunks;
+  const int n_work = hdr->n_tiles * n_hc;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, hh = lane >> 5;
+  const int hf = wave % GF, rb = wave / GF;
+  const int G = a.g.hq / a.g.hkv;
+  const uint32_t qstride = (uint32_t)a.g.hq * D * 2;
+  const uint32_t kstride = (uint32_t)a.g.hkv * D * 2;
+  const uint32_t vstride = (uint32_t)a.g.hkv * DV * 2;
+  const uint32_t ostride = (uint32_t)a.g.hq * DV * 2;
+  const float c = a.scale_log2;
+
+  // DMA slot s of a K (V) tile: row s / CHK (CHV), chunk (s % CH) ^ swizzle
+  uint32_t koff[NDMA_K], voff[NDMA_V];
+#pragma unroll
+  for (int i = 0; i < NDMA_K; ++i) {
+    const int s = (wave + i * NW) * 64 + lane;
+    const int row = s / C::CHK, pc = s % C::CHK;
+    koff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_k<D>(row)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NDMA_V; ++i) {
+    const int s = (wave + i * NW) * 64 + lane;
+    const int row = s / C::CHV, pc = s % C::CHV;
+    voff[i] = (uint32_t)row * vstride + (uint32_t)((pc ^ swz_k<DV>(row)) * 16);
+  }
+  // transposed-read addressing (see read_a_transposed)
+  const int il = lane & 15;
+  const int trow = 4 * hh + (il >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (il & 3);
+
+  const Schedule sch(a.n_cu);
+  for (int r = 0;; ++r) {
+    const int w = sch.item(r);
+    if (w >= n_work) break;
+    sch.priority(r);
+    const int t = (int)((uint32_t)w / (uint32_t)n_hc);
+    const int hc = w - t * n_hc;
+    const int4 tile = a.qws.tiles[t];
+    const int seg = __builtin_amdgcn_readfirstlane(tile.x);
+    const int row0 = __builtin_amdgcn_readfirstlane(tile.y);
+    const int head0 = hc * GF;
+    const int head = head0 + hf;
+    const int kvh = head0 / G;
+    const int q0 = __builtin_amdgcn_readfirstlane(a.g.cu_q[seg]);
+    const int uq = __builtin_amdgcn_readfirstlane(a.g.used_q[seg]);
+    const int k0 = __builtin_amdgcn_readfirstlane(a.g.cu_k[seg]);
+    const int uk = __builtin_amdgcn_readfirstlane(a.g.used_k[seg]);
+    const int wr0 = row0 + rb * 32;
+    const int r_last = min(row0 + 32 * RB, uq) - 1;
+    int kend = uk;
+    if (a.g.causal) kend = max(0, min(uk, r_last + uk - uq + 1));
+    const int n_kt = (kend + 31) / 32;
+
+    const uint32_t qbytes = uq > 0 ? (uint32_t)(uq - 1) * qstride + D * 2 : 0u;
+    const uint32_t obytes = uq > 0 ? (uint32_t)(uq - 1) * ostride + DV * 2 : 0u;
+    const auto qr = make_rsrc(static_cast<const T*>(a.q) + ((int64_t)q0 * a.g.hq + head) * D, qbytes);
+    const auto dor = make_rsrc(static_cast<const T*>(a.dout) + ((int64_t)q0 * a.g.hq + head) * DV, obytes);
+    const auto orr = make_rsrc(static_cast<const T*>(a.o) + ((int64_t)q0 * a.g.hq + head) * DV, obytes);
+    const auto kr = make_rsrc(static_cast<const T*>(a.k) + ((int64_t)k0 * a.g.hkv + kvh) * D,
+                              uk > 0 ? (uint32_t)(uk - 1) * kstride + D * 2 : 0u);
+    const auto vr = make_rsrc(static_cast<const T*>(a.v) + ((int64_t)k0 * a.g.hkv + kvh) * DV,
+                              uk > 0 ? (uint32_t)(uk - 1) * vstride + DV * 2 : 0u);
+
+    auto issue_tile = [&](int kt) {
+      char* st = lds + (kt & 1) * STAGE;
+      const uint32_t ok = (uint32_t)kt * 32 * kstride, ov = (uint32_t)kt * 32 * vstride;
+#pragma unroll
+      for (int i = 0; i < NDMA_K; ++i) {
+        const int inst = wave + i * NW;
+        if (inst < DMA_K) dma16(kr, st + inst * 1024, koff[i] + ok, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NDMA_V; ++i) {
+        const int inst = wave + i * NW;
+        if (inst < DMA_V) dma16(vr, st + K_TILE + inst * 1024, voff[i] + ov, 0);
+      }
+    };
+    if (n_kt > 0) issue_tile(0);
+
+    // this lane's query row: Q and dO fragments, D = rowsum(dO * O)
+    const int row = wr0 + r32;
+    v8 qf[C::KK], df[C::KV];
+    {
+      const uint32_t roff = (uint32_t)row * qstride + hh * 16;
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk)
+        qf[kk] = __builtin_bit_cast(v8, buf_load16(qr, roff + kk * 32));
+    }
+    float dsum = 0.f;
+    {
+      const uint32_t roff = (uint32_t)row * ostride + hh * 16;
+#pragma unroll
+      for (int kk = 0; kk < C::KV; ++kk) {
+        df[kk] = __builtin_bit_cast(v8, buf_load16(dor, roff + kk * 32));
+        const v8 of = __builtin_bit_cast(v8, buf_load16(orr, roff + kk * 32));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dsum = __builtin_fmaf((float)df[kk][j], (float)of[j], dsum);
+      }
+    }
+    dsum = sum_across_halves(dsum);
+    const bool used = row < uq;
+    const float lse = used ? a.lse[(int64_t)head * a.g.total_q + q0 + row] : -INFINITY;
+    // a row without keys (LSE -inf) or past the used rows: P = 0
+    const float lse2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+    if (hh == 0 && used) {
+      float2 st;
+      st.x = lse2;
+      st.y = dsum;
+      reinterpret_cast<float2*>(a.stats)[(int64_t)head * a.g.total_q + q0 + row] = st;
+    }
+
+    f32x16 dq[C::DBK];
+#pragma unroll
+    for (int i = 0; i < C::DBK; ++i) dq[i] = f32x16{};
+    const int lim = a.g.causal ? min(uk, row + uk - uq + 1) : uk;
+    const int lim_w = a.g.causal ? min(uk, wr0 + uk - uq + 1) : uk;
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 < n_kt) issue_tile(kt + 1);
+      const char* Ks = lds + (kt & 1) * STAGE;
+      const char* Vs = Ks + K_TILE;
+
+      // S^T = K Q^T and dP^T = V dO^T: lane (r32, hh) holds query row r32
+      // and keys 8 * (v / 4) + 4 * hh + v % 4 of the tile
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) s = E::mfma(read_a_rows<D, v8>(Ks, r32, hh, kk), qf[kk], s);
+#pragma unroll
+      for (int kk = 0; kk < C::KV; ++kk) dp = E::mfma(read_a_rows<DV, v8>(Vs, r32, hh, kk), df[kk], dp);
+
+      const int kbase = kt * 32;
+      if (kbase + 32 > lim_w) {
+        int nv = lim - kbase - 4 * hh;
+        asm volatile("" : "+v"(nv));
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (8 * (v >> 2) + (v & 3) >= nv) s[v] = -INFINITY;
+      }
+
+      // dS^T = P^T * (dP^T - D) as 16-bit B operands
+      v8 dsb[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = exp2_fast(__builtin_fmaf(s[v], c, -lse2));
+        dsb[v >> 3][v & 7] = (T)(p * (dp[v] - dsum));
+      }
+
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int db = 0; db < C::DBK; ++db)
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2)
+          dq[db] = E::mfma(read_a_transposed<D, v8>(Ks, a2, db * 32, trow, tcol), dsb[a2], dq[db]);
+    }
+
+    // epilogue: scale, stage through LDS, full-row stores of the used rows
+    __syncthreads();
+    T* Ss = reinterpret_cast<T*>(lds) + wave * 32 * C::KP;
+#pragma unroll
+    for (int db = 0; db < C::DBK; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        v4 ov;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) ov[cc] = (T)(dq[db][4 * a4 + cc] * a.scale);
+        *reinterpret_cast<v4*>(Ss + r32 * C::KP + db * 32 + 8 * a4 + 4 * hh) = ov;
+      }
+    __syncthreads();
+    {
+      const auto dqr = make_rsrc(static_cast<T*>(a.dq) + ((int64_t)q0 * a.g.hq + head) * D, qbytes);
+#pragma unroll
+      for (int it = 0; it < D / 16; ++it) {
+        const int idx = it * 64 + lane;
+        const int rr = idx / C::CHK, ch = idx % C::CHK;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(Ss + rr * C::KP + 8 * ch);
+        buf_store16(dqr, (uint32_t)(wr0 + rr) * qstride + ch * 16, val);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV
+// ---------------------------------------------------------------------------
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
+  using C = BwdCfg<D, DV>;
+  using E = Elem<T>;
+  using v8 = typename E::v8;
+  using v4 = typename E::v4;
+  constexpr int NW = 4;
+  constexpr int Q_TILE = 32 * D * 2, O_TILE = 32 * DV * 2, ST_TILE = 32 * 8;
+  constexpr int STAGE = Q_TILE + O_TILE + ST_TILE;
+  constexpr int NDMA_Q = Q_TILE / 1024 / NW, NDMA_O = O_TILE / 1024 / NW;
+  static_assert(NDMA_Q * NW * 1024 == Q_TILE && NDMA_O * NW * 1024 == O_TILE, "DMA split");
+  constexpr int PMAX = C::KP > C::VP ? C::KP : C::VP;
+  constexpr int S_BYTES = NW * 32 * PMAX * 2;
+  constexpr int LDS_BYTES = (2 * STAGE > S_BYTES) ? 2 * STAGE : S_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+
+  const PlanHeader* hdr = a.kws.header;
+  if (hdr->key != a.kkey) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&a.kws.header->err, GVATTN_DEVERR_PLAN);
+    return;
+  }
+  const int hkv = a.g.hkv;
+  const int n_work = hdr->n_tiles * hkv;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, hh = lane >> 5;
+  const int G = a.g.hq / hkv;
+  const uint32_t qstride = (uint32_t)a.g.hq * D * 2;
+  const uint32_t kstride = (uint32_t)hkv * D * 2;
+  const uint32_t vstride = (uint32_t)hkv * DV * 2;
+  const uint32_t ostride = (uint32_t)a.g.hq * DV * 2;
+  const float c = a.scale_log2;
+
+  uint32_t qoff[NDMA_Q], ooff[NDMA_O];
+#pragma unroll
+  for (int i = 0; i < NDMA_Q; ++i) {
+    const int s = (wave + i * NW) * 64 + lane;
+    const int row = s / C::CHK, pc = s % C::CHK;
+    qoff[i] = (uint32_t)row * qstride + (uint32_t)((pc ^ swz_k<D>(row)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NDMA_O; ++i) {
+    const int s = (wave + i * NW) * 64 + lane;
+    const int row = s / C::CHV, pc = s % C::CHV;
+    ooff[i] = (uint32_t)row * ostride + (uint32_t)((pc ^ swz_k<DV>(row)) * 16);
+  }
+  const int il = lane & 15;
+  const int trow = 4 * hh + (il >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (il & 3);
+
+  const Schedule sch(a.n_cu);
+  for (int r = 0;; ++r) {
+    const int w = sch.item(r);
+    if (w >= n_work) break;
+    sch.priority(r);
+    const int t = (int)((uint32_t)w / (uint32_t)hkv);
+    const int kvh = w - t * hkv;
+    const int4 tile = a.kws.tiles[t];
+    const int seg = __builtin_amdgcn_readfirstlane(tile.x);
+    const int k_row0 = __builtin_amdgcn_readfirstlane(tile.y);
+    const int r_first = __builtin_amdgcn_readfirstlane(tile.z);
+    const int q0 = __builtin_amdgcn_readfirstlane(a.g.cu_q[seg]);
+    const int uq = __builtin_amdgcn_readfirstlane(a.g.used_q[seg]);
+    const int k0 = __builtin_amdgcn_readfirstlane(a.g.cu_k[seg]);
+    const int uk = __builtin_amdgcn_readfirstlane(a.g.used_k[seg]);
+    const int wk0 = k_row0 + 32 * wave;  // this wave's first key
+    const int key = wk0 + r32;           // this lane's key (column)
+    const uint32_t kbytes = uk > 0 ? (uint32_t)(uk - 1) * kstride + D * 2 : 0u;
+    const uint32_t vbytes = uk > 0 ? (uint32_t)(uk - 1) * vstride + DV * 2 : 0u;
+    const auto kr = make_rsrc(static_cast<const T*>(a.k) + ((int64_t)k0 * hkv + kvh) * D, kbytes);
+    const auto vr = make_rsrc(static_cast<const T*>(a.v) + ((int64_t)k0 * hkv + kvh) * DV, vbytes);
+
+    // query tiles [qt_first, qt_end) of each of the G heads
+    const int qt_first = r_first / 32;
+    const int qt_end = (uq + 31) / 32;
+    const int n_qt = qt_end - qt_first;
+    const int n_it = G * n_qt;
+    const uint32_t qbytes = uq > 0 ? (uint32_t)(uq - 1) * qstride + D * 2 : 0u;
+    const uint32_t obytes = uq > 0 ? (uint32_t)(uq - 1) * ostride + DV * 2 : 0u;
+    int ld_h = 0, ld_qt = qt_first;  // next (head, query tile) to load
+    auto issue_next = [&](int stage) {
+      const int head = kvh * G + ld_h;
+      char* st = lds + stage * STAGE;
+      const auto qrs = make_rsrc(static_cast<const T*>(a.q) + ((int64_t)q0 * a.g.hq + head) * D, qbytes);
+      const auto ors = make_rsrc(static_cast<const T*>(a.dout) + ((int64_t)q0 * a.g.hq + head) * DV, obytes);
+      const auto srs = make_rsrc(a.stats + ((int64_t)head * a.g.total_q + q0) * 2, (uint32_t)uq * 8u);
+      const uint32_t oq = (uint32_t)ld_qt * 32 * qstride, oo = (uint32_t)ld_qt * 32 * ostride;
+#pragma unroll
+      for (int i = 0; i < NDMA_Q; ++i) dma16(qrs, st + (wave + i * NW) * 1024, qoff[i] + oq, 0);
+#pragma unroll
+      for (int i = 0; i < NDMA_O; ++i) dma16(ors, st + Q_TILE + (wave + i * NW) * 1024, ooff[i] + oo, 0);
+      if (wave == 0 && lane < 64) dma4(srs, st + Q_TILE + O_TILE, (uint32_t)ld_qt * 256u + lane * 4u);
+      if (++ld_qt == qt_end) {
+        ld_qt = qt_first;
+        ++ld_h;
+      }
+    };
+    if (n_it > 0) issue_next(0);
+
+    // K and V fragments of this lane's key (B operands: key = column r32)
+    v8 kf[C::KK], vf[C::KV];
+    {
+      const uint32_t ko = (uint32_t)key * kstride + hh * 16;
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) kf[kk] = __builtin_bit_cast(v8, buf_load16(kr, ko + kk * 32));
+      const uint32_t vo = (uint32_t)key * vstride + hh * 16;
+#pragma unroll
+      for (int kk = 0; kk < C::KV; ++kk) vf[kk] = __builtin_bit_cast(v8, buf_load16(vr, vo + kk * 32));
+    }
+    f32x16 dk[C::DBK], dv[C::DBV];
+#pragma unroll
+    for (int i = 0; i < C::DBK; ++i) dk[i] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < C::DBV; ++i) dv[i] = f32x16{};
+
+    int qt = qt_first;
+    for (int it = 0; it < n_it; ++it) {
+      wait_vmem();
+      __syncthreads();
+      if (it + 1 < n_it) issue_next((it + 1) & 1);
+      const char* Qs = lds + (it & 1) * STAGE;
+      const char* Os = Qs + Q_TILE;
+      const char* Ss = Os + O_TILE;
+      const int qt0 = qt * 32;
+      if (++qt == qt_end) qt = qt_first;
+      // no key of this wave is used, or no row of the tile sees any of them
+      if (wk0 >= uk || (a.g.causal && qt0 + 31 < wk0 + uq - uk)) continue;
+
+      // S = Q K^T and dP = dO V^T: lane (r32, hh) holds key `key` and query
+      // rows qt0 + 8 * (v / 4) + 4 * hh + v % 4
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) s = E::mfma(read_a_rows<D, v8>(Qs, r32, hh, kk), kf[kk], s);
+#pragma unroll
+      for (int kk = 0; kk < C::KV; ++kk) dp = E::mfma(read_a_rows<DV, v8>(Os, r32, hh, kk), vf[kk], dp);
+
+      // per-row (LSE * log2 e, D) of the lane's 16 rows
+      float l2[16], dd[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float* sp = reinterpret_cast<const float*>(Ss) + 2 * (8 * a4 + 4 * hh);
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(sp);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(sp + 4);
+        l2[4 * a4 + 0] = x0[0];
+        dd[4 * a4 + 0] = x0[1];
+        l2[4 * a4 + 1] = x0[2];
+        dd[4 * a4 + 1] = x0[3];
+        l2[4 * a4 + 2] = x1[0];
+        dd[4 * a4 + 2] = x1[1];
+        l2[4 * a4 + 3] = x1[2];
+        dd[4 * a4 + 3] = x1[3];
+      }
+
+      float p[16], ds[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        p[v] = exp2_fast(__builtin_fmaf(s[v], c, -l2[v]));
+        ds[v] = p[v] * (dp[v] - dd[v]);
+      }
+      // masked: key past the used keys, row past the used rows, or (causal)
+      // key after the row's last visible key
+      const bool diag = a.g.causal && wk0 + 31 > qt0 + uk - uq;
+      if (wk0 + 32 > uk || qt0 + 32 > uq || diag) {
+        int lo = a.g.causal ? key - uk + uq - qt0 - 4 * hh : -64;
+        int hi = (key < uk) ? uq - qt0 - 4 * hh : -64;
+        asm volatile("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int cv = 8 * (v >> 2) + (v & 3);
+          if (cv < lo || cv >= hi) {
+            p[v] = 0.f;
+            ds[v] = 0.f;
+          }
+        }
+      }
+      v8 pb[2], dsb[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        pb[v >> 3][v & 7] = (T)p[v];
+        dsb[v >> 3][v & 7] = (T)ds[v];
+      }
+
+      // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+      for (int db = 0; db < C::DBV; ++db)
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2)
+          dv[db] = E::mfma(read_a_transposed<DV, v8>(Os, a2, db * 32, trow, tcol), pb[a2], dv[db]);
+#pragma unroll
+      for (int db = 0; db < C::DBK; ++db)
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2)
+          dk[db] = E::mfma(read_a_transposed<D, v8>(Qs, a2, db * 32, trow, tcol), dsb[a2], dk[db]);
+    }
+
+    // epilogue: dK (scaled) then dV, staged through LDS, rows of used keys
+    T* Ws = reinterpret_cast<T*>(lds) + wave * 32 * PMAX;
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < C::DBK; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        v4 ov;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) ov[cc] = (T)(dk[db][4 * a4 + cc] * a.scale);
+        *reinterpret_cast<v4*>(Ws + r32 * PMAX + db * 32 + 8 * a4 + 4 * hh) = ov;
+      }
+    __syncthreads();
+    {
+      const auto dkr = make_rsrc(static_cast<T*>(a.dk) + ((int64_t)k0 * hkv + kvh) * D, kbytes);
+#pragma unroll
+      for (int it = 0; it < D / 16; ++it) {
+        const int idx = it * 64 + lane;
+        const int rr = idx / C::CHK, ch = idx % C::CHK;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(Ws + rr * PMAX + 8 * ch);
+        buf_store16(dkr, (uint32_t)(wk0 + rr) * kstride + ch * 16, val);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < C::DBV; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        v4 ov;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) ov[cc] = (T)dv[db][4 * a4 + cc];
+        *reinterpret_cast<v4*>(Ws + r32 * PMAX + db * 32 + 8 * a4 + 4 * hh) = ov;
+      }
+    __syncthreads();
+    {
+      const auto dvr = make_rsrc(static_cast<T*>(a.dv) + ((int64_t)k0 * hkv + kvh) * DV, vbytes);
+#pragma unroll
+      for (int it = 0; it < DV / 16; ++it) {
+        const int idx = it * 64 + lane;
+        const int rr = idx / C::CHV, ch = idx % C::CHV;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(Ws + rr * PMAX + 8 * ch);
+        buf_store16(dvr, (uint32_t)(wk0 + rr) * vstride + ch * 16, val);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename K>
+hipError_t launch_persistent(K kern, int threads, int64_t max_work, const BwdArgs& a,
+                             hipStream_t s) {
+  const int grid = persistent_grid(reinterpret_cast<const void*>(kern), threads, max_work);
+  if (grid <= 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DV>
+hipError_t launch_dims(const BwdArgs& a, const TileShape& t, hipStream_t s, bool* ok) {
+  *ok = true;
+  const int64_t q_work = (int64_t)(a.g.total_q / t.rows + a.g.nseg + 1) * a.n_head_chunks;
+  hipError_t e;
+  switch (t.gf) {
+    case 4: e = launch_persistent(bwd_dq_kernel<T, D, DV, 4, 1>, 256, q_work, a, s); break;
+    case 3: e = launch_persistent(bwd_dq_kernel<T, D, DV, 3, 1>, 192, q_work, a, s); break;
+    case 2: e = launch_persistent(bwd_dq_kernel<T, D, DV, 2, 2>, 256, q_work, a, s); break;
+    case 1: e = launch_persistent(bwd_dq_kernel<T, D, DV, 1, 4>, 256, q_work, a, s); break;
+    default: *ok = false; return hipSuccess;
+  }
+  if (e != hipSuccess) return e;
+  const int64_t k_work = (int64_t)(a.g.total_k / kBwdKeyRows + a.g.nseg + 1) * a.g.hkv;
+  return launch_persistent(bwd_dkv_kernel<T, D, DV>, 256, k_work, a, s);
+}
+
+template <typename T>
+hipError_t launch_bwd_t(const BwdArgs& a, const TileShape& t, hipStream_t s, bool* ok) {
+  const int dd = a.g.d, dv = a.g.dv;
+  if (dd == 64 && dv == 64) return launch_dims<T, 64, 64>(a, t, s, ok);
+  if (dd == 64 && dv == 128) return launch_dims<T, 64, 128>(a, t, s, ok);
+  if (dd == 128 && dv == 64) return launch_dims<T, 128, 64>(a, t, s, ok);
+  if (dd == 128 && dv == 128) return launch_dims<T, 128, 128>(a, t, s, ok);
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int dtype, const TileShape& t, hipStream_t s,
+                      bool* supported) {
+  BwdArgs args = a;
+  args.n_cu = device_cu_count();
+  if (args.n_cu <= 0) return hipErrorInvalidValue;
+  if (dtype == GVATTN_BF16) return launch_bwd_t<__bf16>(args, t, s, supported);
+  if (dtype == GVATTN_FP16) return launch_bwd_t<_Float16>(args, t, s, supported);
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace gvattn

@@ -98,13 +98,14 @@ struct WsLayout {
   size_t tiles, seg_off, seg_keys, seg_split, part_o, part_lse, bytes;
 };
 
+// allow_split = false: a plan-only region (the backward's plans).
 inline WsLayout ws_layout(int64_t nseg, int64_t total_q, int hq, int dv, const TileShape& t,
-                          int dtype) {
+                          int dtype, bool allow_split = true) {
   WsLayout L{};
   L.max_tiles = max_tiles(nseg, total_q, t.rows);
   const int64_t items = L.max_tiles * (hq / t.gf);
   L.splits = 1;
-  if (dtype != GVATTN_FP32 && items < kSplitBelow) {
+  if (allow_split && dtype != GVATTN_FP32 && items < kSplitBelow) {
     int64_t s = (kSplitAim + items - 1) / items;
     const int64_t per_split = (int64_t)total_q * hq * (dv + 1) * 4;
     if (per_split > 0 && s * per_split > kSplitBytes) s = kSplitBytes / per_split;
@@ -181,6 +182,7 @@ struct Geometry {
 struct PlanArgs {
   Geometry g;
   WorkspaceView ws;
+  int32_t mode;        // 0: query tiles (forward, dQ); 1: key tiles (dK / dV)
   int32_t rows;        // rows per tile
   int32_t max_tiles;   // query tiles at most (the list holds max_tiles * splits)
   int32_t key_tile;    // keys per key tile of the forward kernel
@@ -204,6 +206,52 @@ struct FwdArgs {
   int32_t n_cu;           // compute units of the device (set by the launcher)
 };
 
+// Backward: the forward's query-tile plan drives the dQ kernel, a key-tile
+// plan (entries: segment, first key row, first query row that sees those
+// keys) drives the dK / dV kernel.  The dQ kernel also writes the per-row
+// statistics the dK / dV kernel reads: (LSE * log2 e, D = rowsum(dO * O))
+// per (head, row), +inf in place of LSE * log2 e for a row without keys.
+struct BwdArgs {
+  Geometry g;
+  WorkspaceView qws;
+  WorkspaceView kws;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* stats;         // [hq, total_q] x 2 floats
+  void* dq;
+  void* dk;
+  void* dv;
+  float scale;
+  float scale_log2;     // scale * log2(e)
+  uint32_t qkey, kkey;
+  int32_t n_head_chunks;  // hq / gf (dQ kernel)
+  int32_t n_cu;
+};
+
+// Workspace of the backward: [query-tile plan][key-tile plan][row stats]
+constexpr int kBwdKeyRows = 128;   // keys per dK / dV work item (4 waves x 32)
+struct BwdLayout {
+  WsLayout q, k;
+  size_t kplan, stats, bytes;
+};
+inline BwdLayout bwd_layout(int64_t nseg, int64_t total_q, int64_t total_k, int hq, int dv,
+                            const TileShape& t, int dtype) {
+  BwdLayout B;
+  B.q = ws_layout(nseg, total_q, hq, dv, t, dtype, false);
+  TileShape tk = t;
+  tk.rows = kBwdKeyRows;
+  tk.gf = 1;
+  B.k = ws_layout(nseg, total_k, hq, dv, tk, dtype, false);
+  B.kplan = align_up(B.q.bytes, 256);
+  B.stats = B.kplan + align_up(B.k.bytes, 256);
+  B.bytes = B.stats + align_up((size_t)hq * total_q * 8, 256);
+  return B;
+}
+
 struct MergeArgs {
   const void* part_out[GVATTN_MAX_PARTS];
   const float* part_lse[GVATTN_MAX_PARTS];
@@ -224,6 +272,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // Combines the split-K partials of the segments the plan split (dtype of
 // the output: GVATTN_BF16 or GVATTN_FP16).
 hipError_t launch_split_merge(const FwdArgs& a, int dtype, hipStream_t s);
+// Backward: dQ (and the row statistics), then dK / dV (dtype GVATTN_BF16 or
+// GVATTN_FP16; d and d_v 64 or 128).  The two plans must have been built.
+hipError_t launch_bwd(const BwdArgs& a, int dtype, const TileShape& t, hipStream_t s,
+                      bool* supported);
 // Matrix-core forward for 16-bit inputs (dtype GVATTN_BF16 or GVATTN_FP16);
 // the key-range form when a.g.kr_off is set.
 hipError_t launch_fwd_mfma(const FwdArgs& a, int dtype, const TileShape& t, int64_t max_work,

@@ -118,6 +118,15 @@ __device__ int tile_key_tiles(const PlanArgs& a, int s, int row0) {
 // (e - e0) / S and key chunk (e - e0) % S of the segment's S = seg_split[s]
 // chunks; the chunk covers key tiles [kt0, kt1) of that query tile.
 __device__ int4 make_entry(const PlanArgs& a, int s, int e0, int e, int* cost) {
+  if (a.mode == 1) {
+    // key tile of `rows` keys: the query rows that see any of its keys
+    // start at r_first (bottom-right causal), cost = their 32-row tiles
+    const int uq = a.g.used_q[s], uk = seg_key_count(a, s);
+    const int k_row0 = (e - e0) * a.rows;
+    const int r_first = a.g.causal ? max(0, min(uq, k_row0 + uq - uk)) : 0;
+    *cost = min((uq - r_first + 31) / 32, kCostBuckets - 1);
+    return make_int4(s, k_row0, r_first, 0);
+  }
   const int S = a.ws.seg_split[s];
   const int local = e - e0;
   const int qt = local / S, j = local - qt * S;
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (s < nseg) {
       const int err = segment_error(a, s);
       if (err) atomicOr(&s_err, err);
-      else cnt = (a.g.used_q[s] + a.rows - 1) / a.rows;
+      else cnt = ((a.mode == 1 ? seg_key_count(a, s) : a.g.used_q[s]) + a.rows - 1) / a.rows;
       a.ws.seg_split[s] = (int32_t)cnt;
     }
     long long tot;
@@ -171,8 +180,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // the whole plan is then rejected (no entries) rather than written past
   // the workspace.
   const long long items = n_qtiles * a.n_head_chunks;
-  const bool split_on = a.ws.splits > 1 && a.g.kr_off == nullptr && items > 0 &&
-                        items < kSplitBelow;
+  const bool split_on = a.mode == 0 && a.ws.splits > 1 && a.g.kr_off == nullptr &&
+                        items > 0 && items < kSplitBelow;
   const int s_aim = split_on ? (int)min((long long)a.ws.splits,
                                         (kSplitAim + items - 1) / items) : 1;
   const long long cap = (long long)a.max_tiles * a.ws.splits;

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for need in ("gvattn_fwd", "gvattn_lse_merge", "gvattn_fwd_plan", "gvattn_fwd_run",
-                 "gvattn_fwd_ranges",
+                 "gvattn_fwd_ranges", "gvattn_bwd", "gvattn_bwd_workspace_size",
                  "gvattn_fwd_workspace_size", "gvattn_status_string",
                  "gvattn_read_device_error", "gvattn_version"):
         assert need in names
@@ -150,6 +150,51 @@ def test_fwd_ranges_host_validation(lib):
     assert _fwd_ranges(lib, ws=FAKE + 16, ws_bytes=ok_ws) == B.GVATTN_ERR_WORKSPACE
     # no ranges at all needs no range arrays (validation only: nseg = 0)
     assert _fwd_ranges(lib, nseg=0, nranges=0, kr_start=None, kr_len=None) == B.GVATTN_OK
+
+
+def _bwd(lib, **over):
+    args = dict(dtype=B.GVATTN_BF16, q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE,
+                cu_q=FAKE, cu_k=FAKE, used_q=FAKE, used_k=FAKE, nseg=4, total_q=1024,
+                total_k=2048, hq=8, hkv=2, d=128, dv=64, scale=0.125, causal=1, dq=FAKE,
+                dk=FAKE, dvv=FAKE, ws=FAKE, ws_bytes=0, stream=None)
+    args.update(over)
+    return lib.gvattn_bwd(*args.values())
+
+
+def test_bwd_workspace_size(lib):
+    n = lib.gvattn_bwd_workspace_size(4, 1024, 2048, 8, 2, 128, 64, B.GVATTN_BF16)
+    assert n > 0 and n % 256 == 0
+    # row statistics: 8 bytes per (query head, query row), so at least that
+    assert n >= 8 * 8 * 1024
+    assert lib.gvattn_bwd_workspace_size(4, 2048, 2048, 8, 2, 128, 64, B.GVATTN_BF16) > n
+    assert lib.gvattn_bwd_workspace_size(4, 1024, 4096, 8, 2, 128, 64, B.GVATTN_BF16) > n
+    assert lib.gvattn_bwd_workspace_size(4, 1024, 2048, 8, 2, 128, 64, B.GVATTN_FP16) == n
+    # the backward is built for 16-bit types and head dims 64 / 128 only
+    assert lib.gvattn_bwd_workspace_size(4, 1024, 2048, 8, 2, 128, 64, B.GVATTN_FP32) == 0
+    assert lib.gvattn_bwd_workspace_size(4, 1024, 2048, 8, 2, 256, 64, B.GVATTN_BF16) == 0
+    assert lib.gvattn_bwd_workspace_size(4, 1024, 2048, 8, 2, 128, 256, B.GVATTN_BF16) == 0
+    assert lib.gvattn_bwd_workspace_size(4, 1024, 2048, 8, 3, 128, 64, B.GVATTN_BF16) == 0
+
+
+def test_bwd_host_validation(lib):
+    ok_ws = lib.gvattn_bwd_workspace_size(4, 1024, 2048, 8, 2, 128, 64, B.GVATTN_BF16)
+    assert _bwd(lib, dtype=B.GVATTN_FP32, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _bwd(lib, dtype=7, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _bwd(lib, d=256, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _bwd(lib, dv=256, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _bwd(lib, d=96, ws_bytes=ok_ws) == B.GVATTN_ERR_UNSUPPORTED
+    assert _bwd(lib, hkv=3, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    assert _bwd(lib, causal=2, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    assert _bwd(lib, scale=0.0, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    assert _bwd(lib, scale=float("nan"), ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    assert _bwd(lib, total_k=-1, ws_bytes=ok_ws) == B.GVATTN_ERR_INVALID_ARG
+    for p in ("q", "k", "v", "out", "dout", "lse", "cu_q", "cu_k", "used_q", "used_k", "dq",
+              "dk", "dvv"):
+        assert _bwd(lib, ws_bytes=ok_ws, **{p: None}) == B.GVATTN_ERR_INVALID_ARG, p
+    assert _bwd(lib, ws=None, ws_bytes=ok_ws) == B.GVATTN_ERR_WORKSPACE
+    assert _bwd(lib, ws=FAKE + 64, ws_bytes=ok_ws) == B.GVATTN_ERR_WORKSPACE
+    assert _bwd(lib, ws_bytes=ok_ws - 1) == B.GVATTN_ERR_WORKSPACE
+    assert _bwd(lib, nseg=0, q=None, ws=None) == B.GVATTN_OK
 
 
 def test_merge_host_validation(lib):

@@ -661,3 +661,54 @@ def test_bwd_gqa_sum_gaps_and_dead_rows():
     # segment 1: 4 rows, 2 keys, bottom-right causal: rows 0 and 1 see nothing
     r0 = int(g.cu_q[1])
     assert np.all(dq[r0:r0 + 2] == 0.0)
+
+
+def test_bwd_magnitudes_bound_the_rounded_backward():
+    """attention_bwd_magnitudes: A_dv is exactly the dV of |dO| (P >= 0);
+    A_dq, A_dk dominate |dQ|, |dK| (triangle inequality); and a backward
+    that rounds P, dS and O to bf16 at the points a 16-bit kernel does
+    stays within 2u (|exact| + A) of the exact gradients (u = 2^-8)."""
+    g, q, k, v, do = _bwd_case(75, [20, 9, 16], [24, 7, 11], [20, 0, 13], [17, 5, 11],
+                               4, 2, 16, 8, True)
+    scale = 0.25
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, g.cu_q, g.cu_k, g.used_q, g.used_k, scale,
+                                      True)
+    a_dq, a_dk, a_dv = oracle.attention_bwd_magnitudes(q, k, v, do, g.cu_q, g.cu_k, g.used_q,
+                                                       g.used_k, scale, True)
+    _, _, dv_abs = oracle.attention_bwd(q, k, v, np.abs(do), g.cu_q, g.cu_k, g.used_q,
+                                        g.used_k, scale, True)
+    assert np.max(np.abs(a_dv - dv_abs)) < 1e-12
+    assert np.all(a_dq >= np.abs(dq) - 1e-12) and np.all(a_dk >= np.abs(dk) - 1e-12)
+
+    def rb(x):
+        return W.round_to_bf16(np.asarray(x, np.float32)).astype(np.float64)
+
+    # the same calculus with P, dS and O rounded to bf16 (everything else exact)
+    rq, rk, rv = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+    rq_no_d = np.zeros_like(dq)
+    for s in range(g.nseg):
+        q0, k0, uq, uk = int(g.cu_q[s]), int(g.cu_k[s]), int(g.used_q[s]), int(g.used_k[s])
+        if uq == 0 or uk == 0:
+            continue
+        i = np.arange(uq)[:, None]
+        vis = np.arange(uk)[None, :] <= i + uk - uq
+        live = vis.any(axis=1)
+        for h in range(4):
+            gk = h // 2
+            sc = np.where(vis, scale * (q[q0:q0 + uq, h] @ k[k0:k0 + uk, gk].T), -np.inf)
+            p = np.zeros_like(sc)
+            e = np.exp(sc[live] - sc[live].max(axis=1, keepdims=True))
+            p[live] = e / e.sum(axis=1, keepdims=True)
+            o = rb(p @ v[k0:k0 + uk, gk])
+            dd = (do[q0:q0 + uq, h] * o).sum(axis=1, keepdims=True)
+            ds = rb(p * (do[q0:q0 + uq, h] @ v[k0:k0 + uk, gk].T - dd))
+            rv[k0:k0 + uk, gk] += rb(p).T @ do[q0:q0 + uq, h]
+            rq[q0:q0 + uq, h] = scale * (ds @ k[k0:k0 + uk, gk])
+            ds_no_d = rb(p * (do[q0:q0 + uq, h] @ v[k0:k0 + uk, gk].T))
+            rq_no_d[q0:q0 + uq, h] = scale * (ds_no_d @ k[k0:k0 + uk, gk])
+            rk[k0:k0 + uk, gk] += scale * (ds.T @ q[q0:q0 + uq, h])
+    u = 2.0 ** -8
+    for r, ex, a in ((rq, dq, a_dq), (rk, dk, a_dk), (rv, dv, a_dv)):
+        assert np.all(np.abs(r - ex) <= 2 * u * (np.abs(ex) + a) + 1e-12)
+    # the bound is not vacuous: dropping D from dS breaks it
+    assert np.any(np.abs(rq_no_d - dq) > 2 * u * (np.abs(dq) + a_dq) + 1e-12)
