@@ -1,7 +1,7 @@
 /*
  * gvattn -- segmented ("gapped") variable-length attention forward, LSE
- * merge and gradients for AMD Instinct MI355X (gfx950).  Plain C ABI: pointers and sizes
- * only, no C++ or framework types.
+ * merge and gradients for AMD Instinct MI355X (gfx950).  Plain C ABI:
+ * pointers and sizes only, no C++ or framework types.
  *
  * The operation (the sources are the pages this library implements):
  *
@@ -241,7 +241,7 @@ const char* gvattn_status_string(int status);
 
 /*
  * Bytes of device workspace gvattn_bwd needs: two plans (query tiles for
- * dQ, 128-key tiles for dK / dV) and 8 bytes of per-row statistics per
+ * dQ, 64-key tiles for dK / dV) and 8 bytes of per-row statistics per
  * (query head, query row).  Depends only on host-known sizes.  Returns 0
  * for invalid or unsupported arguments.
  */

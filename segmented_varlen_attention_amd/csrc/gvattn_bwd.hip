@@ -20,13 +20,14 @@
 //     as the B operand, K^T read transposed (ds_read_b64_tr_b16) from the
 //     row-major K tile.  The kernel also forms D from O and dO and writes
 //     (LSE * log2 e, D) per (head, row) for the second kernel.
-//   * dK / dV: one work item = (128 keys of one segment, KV head) from a
-//     key-tile plan.  Each of 4 waves owns 32 keys with K and V in
-//     registers; the group's query heads and the query tiles that see those
-//     keys stream through LDS.  S = Q K^T and dP = dO V^T leave one key per
-//     lane column, so dV^T += dO^T P and dK^T += Q^T dS take P and dS
-//     straight from the registers; Q^T and dO^T are read transposed from the
-//     row-major tiles.
+//   * dK / dV: one work item = (64 keys of one segment, KV head) from a
+//     key-tile plan.  The group's query heads and the query tiles that see
+//     those keys stream through LDS (Q, dO and the row statistics).  Two
+//     waves share each 32 keys: one holds K and computes S = Q K^T, P and
+//     dV^T += dO^T P; the other holds V and computes dP = dO V^T, takes P
+//     through LDS, forms dS and dK^T += Q^T dS.  Scores leave one key per
+//     lane column, so P and dS are the B operands straight from registers,
+//     and Q^T, dO^T are read transposed from the row-major tiles.
 // Offsets that must be bounds-checked go in the per-lane offset operand of
 // the buffer instructions: loads past a segment's used rows or keys return
 // zero and stores there are dropped, so gap rows of dQ, dK and dV are never
@@ -84,6 +85,11 @@ struct Schedule {
       default: __builtin_amdgcn_s_setprio(3); break;
     }
   }
+};
+
+template <int R>
+struct RoleC {
+  static constexpr int value = R;
 };
 
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
@@ -325,8 +331,15 @@ __global__ __launch_bounds__(64 * GF * RB, 2) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
+// One work item = 64 keys of one segment and KV head.  The 4 waves form two
+// pairs, one pair per 32 keys.  In each pair the "P" wave (role 0) holds K
+// and computes S = Q K^T, P and dV^T += dO^T P; the "dS" wave (role 1) holds
+// V and computes dP = dO V^T, takes P from the P wave through LDS, forms
+// dS = P * (dP - D) and dK^T += Q^T dS.  Each wave holds one fragment set
+// and one accumulator set (two waves per SIMD; the kernel holding both took
+// every register of one).
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
   using C = BwdCfg<D, DV>;
   using E = Elem<T>;
   using v8 = typename E::v8;
@@ -336,9 +349,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int STAGE = Q_TILE + O_TILE + ST_TILE;
   constexpr int NDMA_Q = Q_TILE / 1024 / NW, NDMA_O = O_TILE / 1024 / NW;
   static_assert(NDMA_Q * NW * 1024 == Q_TILE && NDMA_O * NW * 1024 == O_TILE, "DMA split");
+  constexpr int P_BYTES = 64 * 16 * 4;  // one pair's P: 64 lanes x 16 floats
+  constexpr int P_OFF = 2 * STAGE;
   constexpr int PMAX = C::KP > C::VP ? C::KP : C::VP;
   constexpr int S_BYTES = NW * 32 * PMAX * 2;
-  constexpr int LDS_BYTES = (2 * STAGE > S_BYTES) ? 2 * STAGE : S_BYTES;
+  constexpr int MAIN_BYTES = P_OFF + 2 * P_BYTES;
+  constexpr int LDS_BYTES = (MAIN_BYTES > S_BYTES) ? MAIN_BYTES : S_BYTES;
+  constexpr int NF = C::KK > C::KV ? C::KK : C::KV;       // fragment k-steps
+  constexpr int NA = C::DBK > C::DBV ? C::DBK : C::DBV;   // accumulator blocks
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   const PlanHeader* hdr = a.kws.header;
@@ -352,6 +370,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave >> 1, role = wave & 1;
   const int r32 = lane & 31, hh = lane >> 5;
   const int G = a.g.hq / hkv;
   const uint32_t qstride = (uint32_t)a.g.hq * D * 2;
@@ -359,6 +378,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
   const uint32_t vstride = (uint32_t)hkv * DV * 2;
   const uint32_t ostride = (uint32_t)a.g.hq * DV * 2;
   const float c = a.scale_log2;
+  float* Px = reinterpret_cast<float*>(lds + P_OFF + pair * P_BYTES) + lane * 16;
 
   uint32_t qoff[NDMA_Q], ooff[NDMA_O];
 #pragma unroll
@@ -392,14 +412,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int uq = __builtin_amdgcn_readfirstlane(a.g.used_q[seg]);
     const int k0 = __builtin_amdgcn_readfirstlane(a.g.cu_k[seg]);
     const int uk = __builtin_amdgcn_readfirstlane(a.g.used_k[seg]);
-    const int wk0 = k_row0 + 32 * wave;  // this wave's first key
+    const int wk0 = k_row0 + 32 * pair;  // this pair's first key
     const int key = wk0 + r32;           // this lane's key (column)
     const uint32_t kbytes = uk > 0 ? (uint32_t)(uk - 1) * kstride + D * 2 : 0u;
     const uint32_t vbytes = uk > 0 ? (uint32_t)(uk - 1) * vstride + DV * 2 : 0u;
-    const auto kr = make_rsrc(static_cast<const T*>(a.k) + ((int64_t)k0 * hkv + kvh) * D, kbytes);
-    const auto vr = make_rsrc(static_cast<const T*>(a.v) + ((int64_t)k0 * hkv + kvh) * DV, vbytes);
 
-    // query tiles [qt_first, qt_end) of each of the G heads
     const int qt_first = r_first / 32;
     const int qt_end = (uq + 31) / 32;
     const int n_qt = qt_end - qt_first;
@@ -418,7 +435,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
       for (int i = 0; i < NDMA_Q; ++i) dma16(qrs, st + (wave + i * NW) * 1024, qoff[i] + oq, 0);
 #pragma unroll
       for (int i = 0; i < NDMA_O; ++i) dma16(ors, st + Q_TILE + (wave + i * NW) * 1024, ooff[i] + oo, 0);
-      if (wave == 0 && lane < 64) dma4(srs, st + Q_TILE + O_TILE, (uint32_t)ld_qt * 256u + lane * 4u);
+      if (wave == 0) dma4(srs, st + Q_TILE + O_TILE, (uint32_t)ld_qt * 256u + lane * 4u);
       if (++ld_qt == qt_end) {
         ld_qt = qt_first;
         ++ld_h;
@@ -426,144 +443,170 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     };
     if (n_it > 0) issue_next(0);
 
-    // K and V fragments of this lane's key (B operands: key = column r32)
-    v8 kf[C::KK], vf[C::KV];
+    // role 0: K fragments of this lane's key; role 1: V fragments
+    v8 kvf[NF];
     {
-      const uint32_t ko = (uint32_t)key * kstride + hh * 16;
+      const auto kr = make_rsrc(static_cast<const T*>(a.k) + ((int64_t)k0 * hkv + kvh) * D, kbytes);
+      const auto vr = make_rsrc(static_cast<const T*>(a.v) + ((int64_t)k0 * hkv + kvh) * DV, vbytes);
+      if (role == 0) {
+        const uint32_t ko = (uint32_t)key * kstride + hh * 16;
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) kf[kk] = __builtin_bit_cast(v8, buf_load16(kr, ko + kk * 32));
-      const uint32_t vo = (uint32_t)key * vstride + hh * 16;
+        for (int kk = 0; kk < C::KK; ++kk) kvf[kk] = __builtin_bit_cast(v8, buf_load16(kr, ko + kk * 32));
+      } else {
+        const uint32_t vo = (uint32_t)key * vstride + hh * 16;
 #pragma unroll
-      for (int kk = 0; kk < C::KV; ++kk) vf[kk] = __builtin_bit_cast(v8, buf_load16(vr, vo + kk * 32));
+        for (int kk = 0; kk < C::KV; ++kk) kvf[kk] = __builtin_bit_cast(v8, buf_load16(vr, vo + kk * 32));
+      }
     }
-    f32x16 dk[C::DBK], dv[C::DBV];
+    f32x16 acc[NA];
 #pragma unroll
-    for (int i = 0; i < C::DBK; ++i) dk[i] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < C::DBV; ++i) dv[i] = f32x16{};
+    for (int i = 0; i < NA; ++i) acc[i] = f32x16{};
 
-    int qt = qt_first;
-    for (int it = 0; it < n_it; ++it) {
-      wait_vmem();
-      __syncthreads();
-      if (it + 1 < n_it) issue_next((it + 1) & 1);
-      const char* Qs = lds + (it & 1) * STAGE;
-      const char* Os = Qs + Q_TILE;
-      const char* Ss = Os + O_TILE;
-      const int qt0 = qt * 32;
-      if (++qt == qt_end) qt = qt_first;
-      // no key of this wave is used, or no row of the tile sees any of them
-      if (wk0 >= uk || (a.g.causal && qt0 + 31 < wk0 + uq - uk)) continue;
+    // one copy of the loop per role, so that each is register-allocated on
+    // its own
+    auto iterate = [&](auto role_c) {
+      constexpr int R = decltype(role_c)::value;
+      int qt = qt_first;
+      for (int it = 0; it < n_it; ++it) {
+        wait_vmem();
+        __syncthreads();
+        if (it + 1 < n_it) issue_next((it + 1) & 1);
+        const char* Qs = lds + (it & 1) * STAGE;
+        const char* Os = Qs + Q_TILE;
+        const float* Ss = reinterpret_cast<const float*>(Os + O_TILE);
+        const int qt0 = qt * 32;
+        if (++qt == qt_end) qt = qt_first;
+        // no key of this pair is used, or no row of the tile sees any of them
+        const bool skip = wk0 >= uk || (a.g.causal && qt0 + 31 < wk0 + uq - uk);
+        // masked: key past the used keys, row past the used rows, or (causal)
+        // key after the row's last visible key
+        const bool edge = wk0 + 32 > uk || qt0 + 32 > uq || (a.g.causal && wk0 + 31 > qt0 + uk - uq);
 
-      // S = Q K^T and dP = dO V^T: lane (r32, hh) holds key `key` and query
-      // rows qt0 + 8 * (v / 4) + 4 * hh + v % 4
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) s = E::mfma(read_a_rows<D, v8>(Qs, r32, hh, kk), kf[kk], s);
-#pragma unroll
-      for (int kk = 0; kk < C::KV; ++kk) dp = E::mfma(read_a_rows<DV, v8>(Os, r32, hh, kk), vf[kk], dp);
-
-      // per-row (LSE * log2 e, D) of the lane's 16 rows
-      float l2[16], dd[16];
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const float* sp = reinterpret_cast<const float*>(Ss) + 2 * (8 * a4 + 4 * hh);
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(sp);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(sp + 4);
-        l2[4 * a4 + 0] = x0[0];
-        dd[4 * a4 + 0] = x0[1];
-        l2[4 * a4 + 1] = x0[2];
-        dd[4 * a4 + 1] = x0[3];
-        l2[4 * a4 + 2] = x1[0];
-        dd[4 * a4 + 2] = x1[1];
-        l2[4 * a4 + 3] = x1[2];
-        dd[4 * a4 + 3] = x1[3];
-      }
-
-      float p[16], ds[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[v] = exp2_fast(__builtin_fmaf(s[v], c, -l2[v]));
-        ds[v] = p[v] * (dp[v] - dd[v]);
-      }
-      // masked: key past the used keys, row past the used rows, or (causal)
-      // key after the row's last visible key
-      const bool diag = a.g.causal && wk0 + 31 > qt0 + uk - uq;
-      if (wk0 + 32 > uk || qt0 + 32 > uq || diag) {
-        int lo = a.g.causal ? key - uk + uq - qt0 - 4 * hh : -64;
-        int hi = (key < uk) ? uq - qt0 - 4 * hh : -64;
-        asm volatile("" : "+v"(lo), "+v"(hi));
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int cv = 8 * (v >> 2) + (v & 3);
-          if (cv < lo || cv >= hi) {
-            p[v] = 0.f;
-            ds[v] = 0.f;
+        // lane (r32, hh) holds key `key` and query rows
+        // qt0 + 8 * (v / 4) + 4 * hh + v % 4 of the tile
+        v8 opb[2];
+        if (!skip) {
+          if constexpr (R == 0) {
+            f32x16 s = f32x16{};
+  #pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk) s = E::mfma(read_a_rows<D, v8>(Qs, r32, hh, kk), kvf[kk], s);
+  #pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const f32x4 x0 = *reinterpret_cast<const f32x4*>(Ss + 2 * (8 * a4 + 4 * hh));
+              const f32x4 x1 = *reinterpret_cast<const f32x4*>(Ss + 2 * (8 * a4 + 4 * hh) + 4);
+              s[4 * a4 + 0] = exp2_fast(__builtin_fmaf(s[4 * a4 + 0], c, -x0[0]));
+              s[4 * a4 + 1] = exp2_fast(__builtin_fmaf(s[4 * a4 + 1], c, -x0[2]));
+              s[4 * a4 + 2] = exp2_fast(__builtin_fmaf(s[4 * a4 + 2], c, -x1[0]));
+              s[4 * a4 + 3] = exp2_fast(__builtin_fmaf(s[4 * a4 + 3], c, -x1[2]));
+            }
+            if (edge) {
+              int lo = a.g.causal ? key - uk + uq - qt0 - 4 * hh : -64;
+              int hi = (key < uk) ? uq - qt0 - 4 * hh : -64;
+              asm volatile("" : "+v"(lo), "+v"(hi));
+  #pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int cv = 8 * (v >> 2) + (v & 3);
+                if (cv < lo || cv >= hi) s[v] = 0.f;
+              }
+            }
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              f32x4 x;
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) x[j] = s[4 * i + j];
+              *reinterpret_cast<f32x4*>(Px + 4 * i) = x;
+            }
+  #pragma unroll
+            for (int v = 0; v < 16; ++v) opb[v >> 3][v & 7] = (T)s[v];
+          } else {
+            f32x16 dp = f32x16{};
+  #pragma unroll
+            for (int kk = 0; kk < C::KV; ++kk) dp = E::mfma(read_a_rows<DV, v8>(Os, r32, hh, kk), kvf[kk], dp);
+  #pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const f32x4 x0 = *reinterpret_cast<const f32x4*>(Ss + 2 * (8 * a4 + 4 * hh));
+              const f32x4 x1 = *reinterpret_cast<const f32x4*>(Ss + 2 * (8 * a4 + 4 * hh) + 4);
+              dp[4 * a4 + 0] -= x0[1];
+              dp[4 * a4 + 1] -= x0[3];
+              dp[4 * a4 + 2] -= x1[1];
+              dp[4 * a4 + 3] -= x1[3];
+            }
+            __syncthreads();  // P of this tile is in LDS
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x4 x = *reinterpret_cast<const f32x4*>(Px + 4 * i);
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) dp[4 * i + j] *= x[j];
+            }
+            if (edge) {
+              int lo = a.g.causal ? key - uk + uq - qt0 - 4 * hh : -64;
+              int hi = (key < uk) ? uq - qt0 - 4 * hh : -64;
+              asm volatile("" : "+v"(lo), "+v"(hi));
+  #pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int cv = 8 * (v >> 2) + (v & 3);
+                if (cv < lo || cv >= hi) dp[v] = 0.f;
+              }
+            }
+  #pragma unroll
+            for (int v = 0; v < 16; ++v) opb[v >> 3][v & 7] = (T)dp[v];
           }
         }
-      }
-      v8 pb[2], dsb[2];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        pb[v >> 3][v & 7] = (T)p[v];
-        dsb[v >> 3][v & 7] = (T)ds[v];
-      }
+        if (R == 0 || skip) __syncthreads();  // pairs with the dS wave's wait
+        // a skipped tile adds zero products: the accumulators then stay in
+        // place instead of being merged from two paths
+        if (skip) opb[0] = opb[1] = v8{};
 
-      // dV^T += dO^T P and dK^T += Q^T dS
-#pragma unroll
-      for (int db = 0; db < C::DBV; ++db)
-#pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2)
-          dv[db] = E::mfma(read_a_transposed<DV, v8>(Os, a2, db * 32, trow, tcol), pb[a2], dv[db]);
-#pragma unroll
-      for (int db = 0; db < C::DBK; ++db)
-#pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2)
-          dk[db] = E::mfma(read_a_transposed<D, v8>(Qs, a2, db * 32, trow, tcol), dsb[a2], dk[db]);
-    }
+        // role 0: dV^T += dO^T P;  role 1: dK^T += Q^T dS
+        if constexpr (R == 0) {
+  #pragma unroll
+          for (int db = 0; db < C::DBV; ++db)
+  #pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+              acc[db] = E::mfma(read_a_transposed<DV, v8>(Os, a2, db * 32, trow, tcol), opb[a2], acc[db]);
+        } else {
+  #pragma unroll
+          for (int db = 0; db < C::DBK; ++db)
+  #pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+              acc[db] = E::mfma(read_a_transposed<D, v8>(Qs, a2, db * 32, trow, tcol), opb[a2], acc[db]);
+        }
+      }
+    };
+    if (role == 0) iterate(RoleC<0>{});
+    else iterate(RoleC<1>{});
 
-    // epilogue: dK (scaled) then dV, staged through LDS, rows of used keys
+    // epilogue: role 0 writes dV, role 1 writes dK (scaled), rows of used
+    // keys, staged through LDS
     T* Ws = reinterpret_cast<T*>(lds) + wave * 32 * PMAX;
     __syncthreads();
+    const int width = role == 0 ? DV : D;
+    const float f = role == 0 ? 1.f : a.scale;
 #pragma unroll
-    for (int db = 0; db < C::DBK; ++db)
+    for (int db = 0; db < NA; ++db)
+      if (db * 32 < width)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        v4 ov;
+        for (int a4 = 0; a4 < 4; ++a4) {
+          v4 ov;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) ov[cc] = (T)(dk[db][4 * a4 + cc] * a.scale);
-        *reinterpret_cast<v4*>(Ws + r32 * PMAX + db * 32 + 8 * a4 + 4 * hh) = ov;
-      }
+          for (int cc = 0; cc < 4; ++cc) ov[cc] = (T)(acc[db][4 * a4 + cc] * f);
+          *reinterpret_cast<v4*>(Ws + r32 * PMAX + db * 32 + 8 * a4 + 4 * hh) = ov;
+        }
     __syncthreads();
     {
-      const auto dkr = make_rsrc(static_cast<T*>(a.dk) + ((int64_t)k0 * hkv + kvh) * D, kbytes);
+      const uint32_t stride = role == 0 ? vstride : kstride;
+      const auto orr = (role == 0)
+          ? make_rsrc(static_cast<T*>(a.dv) + ((int64_t)k0 * hkv + kvh) * DV, vbytes)
+          : make_rsrc(static_cast<T*>(a.dk) + ((int64_t)k0 * hkv + kvh) * D, kbytes);
+      const int ch_row = width / 8;
 #pragma unroll
-      for (int it = 0; it < D / 16; ++it) {
+      for (int it = 0; it < (D > DV ? D : DV) / 16; ++it) {
         const int idx = it * 64 + lane;
-        const int rr = idx / C::CHK, ch = idx % C::CHK;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(Ws + rr * PMAX + 8 * ch);
-        buf_store16(dkr, (uint32_t)(wk0 + rr) * kstride + ch * 16, val);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int db = 0; db < C::DBV; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        v4 ov;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) ov[cc] = (T)dv[db][4 * a4 + cc];
-        *reinterpret_cast<v4*>(Ws + r32 * PMAX + db * 32 + 8 * a4 + 4 * hh) = ov;
-      }
-    __syncthreads();
-    {
-      const auto dvr = make_rsrc(static_cast<T*>(a.dv) + ((int64_t)k0 * hkv + kvh) * DV, vbytes);
-#pragma unroll
-      for (int it = 0; it < DV / 16; ++it) {
-        const int idx = it * 64 + lane;
-        const int rr = idx / C::CHV, ch = idx % C::CHV;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(Ws + rr * PMAX + 8 * ch);
-        buf_store16(dvr, (uint32_t)(wk0 + rr) * vstride + ch * 16, val);
+        const int rr = idx / ch_row, ch = idx % ch_row;
+        if (rr < 32) {
+          const u32x4 val = *reinterpret_cast<const u32x4*>(Ws + rr * PMAX + 8 * ch);
+          buf_store16(orr, (uint32_t)(wk0 + rr) * stride + ch * 16, val);
+        }
       }
     }
     __syncthreads();

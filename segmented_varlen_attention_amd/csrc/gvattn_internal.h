@@ -233,7 +233,7 @@ struct BwdArgs {
 };
 
 // Workspace of the backward: [query-tile plan][key-tile plan][row stats]
-constexpr int kBwdKeyRows = 128;   // keys per dK / dV work item (4 waves x 32)
+constexpr int kBwdKeyRows = 64;    // keys per dK / dV work item (2 wave pairs x 32)
 struct BwdLayout {
   WsLayout q, k;
   size_t kplan, stats, bytes;
