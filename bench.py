@@ -41,12 +41,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the translation unit of the attention forward kernel the counters cover
+FWD_SOURCES = ("gvattn_fwd_mfma.hip", "gvattn_mfma.h", "gvattn_internal.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in FWD_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    with open(os.path.join(ROOT, "include", "gvattn.h"), "rb") as fh:
+        h.update(b"gvattn.h\0" + fh.read())
     return h.hexdigest()[:16]
 
 
