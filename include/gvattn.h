@@ -241,9 +241,10 @@ const char* gvattn_status_string(int status);
 
 /*
  * Bytes of device workspace gvattn_bwd needs: two plans (query tiles for
- * dQ, 64-key tiles for dK / dV) and 8 bytes of per-row statistics per
- * (query head, query row).  Depends only on host-known sizes.  Returns 0
- * for invalid or unsupported arguments.
+ * dQ, 64-key tiles for dK / dV), 8 bytes of per-row statistics per (query
+ * head, query row) and FP32 partials for launches with few key tiles (at
+ * most 1024 x 64 x (d + d_v) x 4 bytes).  Depends only on host-known sizes.
+ * Returns 0 for invalid or unsupported arguments.
  */
 size_t gvattn_bwd_workspace_size(int32_t nseg, int32_t total_q, int32_t total_k,
                                  int32_t hq, int32_t hkv, int32_t d, int32_t d_v,

@@ -127,6 +127,7 @@ int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
   a.g = g;
   a.ws = view_workspace(ws, L);
   a.mode = 0;
+  a.part_slots = 0;
   a.rows = t.rows;
   a.max_tiles = (int32_t)L.max_tiles;
   a.key_tile = key_tile(g.d, g.dv);
@@ -192,7 +193,7 @@ int check_bwd_sizes(int32_t dtype, int32_t nseg, int32_t total_q, int32_t total_
 
 BwdLayout bwd_layout_of(int32_t dtype, int32_t nseg, int32_t total_q, int32_t total_k,
                         int32_t hq, int32_t hkv, int32_t d, int32_t dv) {
-  return bwd_layout(nseg, total_q, total_k, hq, dv, choose_shape(dtype, hq, hkv, d), dtype);
+  return bwd_layout(nseg, total_q, total_k, hq, hkv, d, dv, choose_shape(dtype, hq, hkv, d), dtype);
 }
 
 int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const void* v,
@@ -208,6 +209,7 @@ int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   pq.g = g;
   pq.ws = view_workspace(base, L.q);
   pq.mode = 0;
+  pq.part_slots = 0;
   pq.rows = t.rows;
   pq.max_tiles = (int32_t)L.q.max_tiles;
   pq.key_tile = 32;
@@ -218,6 +220,7 @@ int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   PlanArgs pk = pq;
   pk.ws = view_workspace(base + L.kplan, L.k);
   pk.mode = 1;
+  pk.part_slots = L.part_slots;
   pk.rows = kBwdKeyRows;
   pk.max_tiles = (int32_t)L.k.max_tiles;
   pk.n_head_chunks = g.hkv;
@@ -236,6 +239,8 @@ int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   b.dout = dout;
   b.lse = lse;
   b.stats = reinterpret_cast<float*>(base + L.stats);
+  b.kpart = reinterpret_cast<float*>(base + L.kpart);
+  b.kpart_slots = L.part_slots;
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;

@@ -420,10 +420,26 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
     const int qt_first = r_first / 32;
     const int qt_end = (uq + 31) / 32;
     const int n_qt = qt_end - qt_first;
-    const int n_it = G * n_qt;
+    // steps [it0, it0 + n_it) of the (query head, query tile) loop: all of
+    // them, or chunk j of a split item, whose sums go to partial slot
+    // `slot` (the reduce pass adds the chunks)
+    const int wfield = __builtin_amdgcn_readfirstlane(tile.w);
+    const bool partial = wfield & 1;
+    const int slot = (int)((uint32_t)wfield >> 5);
+    int it0 = 0, n_it = G * n_qt;
+    if (partial) {
+      const int n_all = n_it;
+      const int S = __builtin_amdgcn_readfirstlane(a.kws.seg_split[seg]);
+      const int chunk = (n_all + S - 1) / S;
+      it0 = min(((wfield >> 1) & 15) * chunk, n_all);
+      n_it = min(it0 + chunk, n_all) - it0;
+    }
     const uint32_t qbytes = uq > 0 ? (uint32_t)(uq - 1) * qstride + D * 2 : 0u;
     const uint32_t obytes = uq > 0 ? (uint32_t)(uq - 1) * ostride + DV * 2 : 0u;
-    int ld_h = 0, ld_qt = qt_first;  // next (head, query tile) to load
+    // next (head, query tile) to load
+    int ld_h = n_qt > 0 ? it0 / n_qt : 0;
+    int ld_qt = qt_first + (it0 - ld_h * n_qt);
+    const int qt_start = ld_qt;
     auto issue_next = [&](int stage) {
       const int head = kvh * G + ld_h;
       char* st = lds + stage * STAGE;
@@ -466,7 +482,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
     // its own
     auto iterate = [&](auto role_c) {
       constexpr int R = decltype(role_c)::value;
-      int qt = qt_first;
+      int qt = qt_start;
       for (int it = 0; it < n_it; ++it) {
         wait_vmem();
         __syncthreads();
@@ -576,6 +592,26 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
     if (role == 0) iterate(RoleC<0>{});
     else iterate(RoleC<1>{});
 
+    if (partial) {
+      // FP32 sums of this chunk: [64 keys][d + d_v] per (slot, KV head),
+      // dK (unscaled) in columns [0, d), dV in [d, d + d_v)
+      float* pp = a.kpart + ((int64_t)slot * hkv + kvh) * (kBwdKeyRows * (D + DV)) +
+                  (pair * 32 + r32) * (D + DV) + (role == 0 ? D : 0);
+      const int width = role == 0 ? DV : D;
+#pragma unroll
+      for (int db = 0; db < NA; ++db)
+        if (db * 32 < width)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            f32x4 x;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) x[cc] = acc[db][4 * a4 + cc];
+            *reinterpret_cast<f32x4*>(pp + db * 32 + 8 * a4 + 4 * hh) = x;
+          }
+      __syncthreads();  // the next item's loads reuse the stages
+      continue;
+    }
+
     // epilogue: role 0 writes dV, role 1 writes dK (scaled), rows of used
     // keys, staged through LDS
     T* Ws = reinterpret_cast<T*>(lds) + wave * 32 * PMAX;
@@ -614,6 +650,48 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dK / dV of split items: sum of the chunks' FP32 partials
+// ---------------------------------------------------------------------------
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a) {
+  const PlanHeader* hdr = a.kws.header;
+  if (hdr->key != a.kkey) return;  // the dK / dV kernel reported it
+  const int hkv = a.g.hkv;
+  const int n_work = hdr->n_tiles * hkv;
+  constexpr int W = D + DV;
+  constexpr int C4 = W / 4;  // float4 columns per key row
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+    const int t = w / hkv, kvh = w - t * hkv;
+    const int4 tile = a.kws.tiles[t];
+    // chunk 0 of a split item reduces it; its slot is the first of S
+    if (!(tile.w & 1) || ((tile.w >> 1) & 15) != 0) continue;
+    const int seg = tile.x, k_row0 = tile.y;
+    const int slot0 = (int)((uint32_t)tile.w >> 5);
+    const int S = a.kws.seg_split[seg];
+    const int k0 = a.g.cu_k[seg], uk = a.g.used_k[seg];
+    for (int i = threadIdx.x; i < kBwdKeyRows * C4; i += blockDim.x) {
+      const int kr = i / C4, c4 = i - kr * C4;
+      if (k_row0 + kr >= uk) continue;
+      f32x4 sum = f32x4{};
+      for (int j = 0; j < S; ++j)
+        sum += *reinterpret_cast<const f32x4*>(
+            a.kpart + (((int64_t)(slot0 + j) * hkv + kvh) * kBwdKeyRows + kr) * W + 4 * c4);
+      const int64_t row = (int64_t)(k0 + k_row0 + kr) * hkv + kvh;
+      typename Elem<T>::v4 o;
+      if (4 * c4 < D) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) o[cc] = (T)(sum[cc] * a.scale);
+        *reinterpret_cast<typename Elem<T>::v4*>(static_cast<T*>(a.dk) + row * D + 4 * c4) = o;
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) o[cc] = (T)sum[cc];
+        *reinterpret_cast<typename Elem<T>::v4*>(static_cast<T*>(a.dv) + row * DV + 4 * c4 - D) = o;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <typename K>
@@ -638,8 +716,19 @@ hipError_t launch_dims(const BwdArgs& a, const TileShape& t, hipStream_t s, bool
     default: *ok = false; return hipSuccess;
   }
   if (e != hipSuccess) return e;
-  const int64_t k_work = (int64_t)(a.g.total_k / kBwdKeyRows + a.g.nseg + 1) * a.g.hkv;
-  return launch_persistent(bwd_dkv_kernel<T, D, DV>, 256, k_work, a, s);
+  const int64_t k_work =
+      (int64_t)(a.g.total_k / kBwdKeyRows + a.g.nseg + 1) * a.g.hkv * kMaxSplits;
+  e = launch_persistent(bwd_dkv_kernel<T, D, DV>, 256, k_work, a, s);
+  if (e != hipSuccess) return e;
+  // walks the work list and reduces the split items (none: it only scans)
+  const int64_t r_work = a.kpart_slots > 0 ? k_work : 0;
+  const int grid = (int)(r_work < 2048 ? r_work : 2048);
+  if (grid > 0) {
+    auto reduce = bwd_kv_reduce_kernel<T, D, DV>;
+    hipLaunchKernelGGL(reduce, dim3(grid), dim3(256), 0, s, a);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <typename T>

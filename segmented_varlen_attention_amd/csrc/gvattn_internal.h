@@ -98,13 +98,15 @@ struct WsLayout {
   size_t tiles, seg_off, seg_keys, seg_split, part_o, part_lse, bytes;
 };
 
-// allow_split = false: a plan-only region (the backward's plans).
+// allow_split = false: a plan-only region (the backward's plans), whose work
+// list holds list_splits entries per tile (chunks whose partials live
+// elsewhere).
 inline WsLayout ws_layout(int64_t nseg, int64_t total_q, int hq, int dv, const TileShape& t,
-                          int dtype, bool allow_split = true) {
+                          int dtype, bool allow_split = true, int list_splits = 1) {
   WsLayout L{};
   L.max_tiles = max_tiles(nseg, total_q, t.rows);
   const int64_t items = L.max_tiles * (hq / t.gf);
-  L.splits = 1;
+  L.splits = allow_split ? 1 : list_splits;
   if (allow_split && dtype != GVATTN_FP32 && items < kSplitBelow) {
     int64_t s = (kSplitAim + items - 1) / items;
     const int64_t per_split = (int64_t)total_q * hq * (dv + 1) * 4;
@@ -121,7 +123,7 @@ inline WsLayout ws_layout(int64_t nseg, int64_t total_q, int hq, int dv, const T
   L.seg_split = b;
   b += align_up((size_t)(nseg + 1) * 4, 256);
   L.part_o = L.part_lse = 0;
-  if (L.splits > 1) {
+  if (allow_split && L.splits > 1) {
     L.part_o = b;
     b += align_up((size_t)L.splits * total_q * hq * dv * 4, 256);
     L.part_lse = b;
@@ -150,8 +152,8 @@ inline WorkspaceView view_workspace(void* ws, const WsLayout& L) {
   v.seg_tile_off = reinterpret_cast<int32_t*>(p + L.seg_off);
   v.seg_keys = reinterpret_cast<int32_t*>(p + L.seg_keys);
   v.seg_split = reinterpret_cast<int32_t*>(p + L.seg_split);
-  v.part_o = L.splits > 1 ? reinterpret_cast<float*>(p + L.part_o) : nullptr;
-  v.part_lse = L.splits > 1 ? reinterpret_cast<float*>(p + L.part_lse) : nullptr;
+  v.part_o = L.part_o ? reinterpret_cast<float*>(p + L.part_o) : nullptr;
+  v.part_lse = L.part_lse ? reinterpret_cast<float*>(p + L.part_lse) : nullptr;
   v.splits = L.splits;
   return v;
 }
@@ -183,6 +185,7 @@ struct PlanArgs {
   Geometry g;
   WorkspaceView ws;
   int32_t mode;        // 0: query tiles (forward, dQ); 1: key tiles (dK / dV)
+  int32_t part_slots;  // mode 1: (entry, KV head) partials available for splits
   int32_t rows;        // rows per tile
   int32_t max_tiles;   // query tiles at most (the list holds max_tiles * splits)
   int32_t key_tile;    // keys per key tile of the forward kernel
@@ -222,6 +225,8 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   float* stats;         // [hq, total_q] x 2 floats
+  float* kpart;         // split dK / dV partials: [slot][hkv][64 keys][d + d_v] fp32
+  int32_t kpart_slots;  // (slot, KV head) pairs kpart holds
   void* dq;
   void* dk;
   void* dv;
@@ -233,22 +238,35 @@ struct BwdArgs {
 };
 
 // Workspace of the backward: [query-tile plan][key-tile plan][row stats]
+// [dK / dV partials].  A launch with fewer than kBwdSplitBelow dK / dV items
+// (key tiles x KV heads) splits each item's (query head, query tile) loop
+// into up to kMaxSplits chunks of at least kBwdMinChunk iterations, aiming
+// at kBwdSplitAim items; each chunk writes FP32 partials into one of
+// part_slots (entry, KV head) slots and a reduce pass sums them.
 constexpr int kBwdKeyRows = 64;    // keys per dK / dV work item (2 wave pairs x 32)
+constexpr int kBwdSplitBelow = 384;
+constexpr int kBwdSplitAim = 1536;
+constexpr int kBwdMinChunk = 8;
+constexpr int kBwdPartSlots = 1024;
 struct BwdLayout {
   WsLayout q, k;
-  size_t kplan, stats, bytes;
+  int32_t part_slots;
+  size_t kplan, stats, kpart, bytes;
 };
-inline BwdLayout bwd_layout(int64_t nseg, int64_t total_q, int64_t total_k, int hq, int dv,
-                            const TileShape& t, int dtype) {
+inline BwdLayout bwd_layout(int64_t nseg, int64_t total_q, int64_t total_k, int hq, int hkv,
+                            int d, int dv, const TileShape& t, int dtype) {
   BwdLayout B;
   B.q = ws_layout(nseg, total_q, hq, dv, t, dtype, false);
   TileShape tk = t;
   tk.rows = kBwdKeyRows;
   tk.gf = 1;
-  B.k = ws_layout(nseg, total_k, hq, dv, tk, dtype, false);
+  B.k = ws_layout(nseg, total_k, hq, dv, tk, dtype, false, kMaxSplits);
+  const int64_t slots = B.k.max_tiles * hkv * kMaxSplits;
+  B.part_slots = (int32_t)(slots < kBwdPartSlots ? slots : kBwdPartSlots);
   B.kplan = align_up(B.q.bytes, 256);
   B.stats = B.kplan + align_up(B.k.bytes, 256);
-  B.bytes = B.stats + align_up((size_t)hq * total_q * 8, 256);
+  B.kpart = B.stats + align_up((size_t)hq * total_q * 8, 256);
+  B.bytes = B.kpart + align_up((size_t)B.part_slots * kBwdKeyRows * (d + dv) * 4, 256);
   return B;
 }
 

@@ -120,12 +120,25 @@ __device__ int tile_key_tiles(const PlanArgs& a, int s, int row0) {
 __device__ int4 make_entry(const PlanArgs& a, int s, int e0, int e, int* cost) {
   if (a.mode == 1) {
     // key tile of `rows` keys: the query rows that see any of its keys
-    // start at r_first (bottom-right causal), cost = their 32-row tiles
+    // start at r_first (bottom-right causal); its loop runs over (query
+    // head, 32-row query tile), split into S chunks when the segment's
+    // seg_split S > 1 (chunk j of key tile kt is entry e0 + kt * S + j, and
+    // e names its partial slot)
+    const int S = a.ws.seg_split[s];
+    const int local = e - e0;
+    const int kt = local / S, j = local - kt * S;
     const int uq = a.g.used_q[s], uk = seg_key_count(a, s);
-    const int k_row0 = (e - e0) * a.rows;
+    const int k_row0 = kt * a.rows;
     const int r_first = a.g.causal ? max(0, min(uq, k_row0 + uq - uk)) : 0;
-    *cost = min((uq - r_first + 31) / 32, kCostBuckets - 1);
-    return make_int4(s, k_row0, r_first, 0);
+    const int n_it = (a.g.hq / a.g.hkv) * ((uq + 31) / 32 - r_first / 32);
+    int it0 = 0, it1 = n_it;
+    if (S > 1) {
+      const int chunk = (n_it + S - 1) / S;
+      it0 = min(j * chunk, n_it);
+      it1 = min(it0 + chunk, n_it);
+    }
+    *cost = min(it1 - it0, kCostBuckets - 1);
+    return make_int4(s, k_row0, r_first, (e << 5) | (j << 1) | (S > 1 ? 1 : 0));
   }
   const int S = a.ws.seg_split[s];
   const int local = e - e0;
@@ -180,10 +193,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // the whole plan is then rejected (no entries) rather than written past
   // the workspace.
   const long long items = n_qtiles * a.n_head_chunks;
-  const bool split_on = a.mode == 0 && a.ws.splits > 1 && a.g.kr_off == nullptr &&
-                        items > 0 && items < kSplitBelow;
-  const int s_aim = split_on ? (int)min((long long)a.ws.splits,
-                                        (kSplitAim + items - 1) / items) : 1;
+  const bool split_on =
+      a.mode == 0 ? (a.ws.splits > 1 && a.g.kr_off == nullptr && items > 0 && items < kSplitBelow)
+                  : (a.ws.splits > 1 && items > 0 && items < kBwdSplitBelow &&
+                     a.part_slots >= 2 * items);
+  int s_aim = 1;
+  if (split_on && a.mode == 0)
+    s_aim = (int)min((long long)a.ws.splits, (kSplitAim + items - 1) / items);
+  else if (split_on)  // every (entry, KV head) chunk needs a partial slot
+    s_aim = (int)min(min((long long)a.ws.splits, (kBwdSplitAim + items - 1) / items),
+                     (long long)a.part_slots / items);
   const long long cap = (long long)a.max_tiles * a.ws.splits;
   long long carry = 0;
   for (int base = 0; base < nseg; base += kPlanThreads) {
@@ -193,8 +212,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int qt = a.ws.seg_split[s];
       int S = 1;
       if (split_on && qt > 0) {
-        const int kt = (seg_key_count(a, s) + a.key_tile - 1) / a.key_tile;
-        S = max(1, min(s_aim, kt / kMinSplitTiles));
+        if (a.mode == 0) {
+          const int kt = (seg_key_count(a, s) + a.key_tile - 1) / a.key_tile;
+          S = max(1, min(s_aim, kt / kMinSplitTiles));
+        } else {  // chunks of at least kBwdMinChunk (head, query tile) steps
+          const int steps = (a.g.hq / a.g.hkv) * ((a.g.used_q[s] + 31) / 32);
+          S = max(1, min(s_aim, steps / kBwdMinChunk));
+        }
       }
       a.ws.seg_split[s] = S;
       if (S > 1) atomicMax(&s_max_split, S);

@@ -227,3 +227,13 @@ def test_bwd_causal_replay_full_size_sampled():
             m = np.ones(want.shape[0], dtype=bool)
             st[name] = check_grad(to_np(got), want, mag, m, W.BF16, f"config3 seg {s} {name}")
         say(f"[bwd config3] seg {s}", st)
+
+
+def test_bwd_cross_attention_split():
+    """The CFG cross-attention workload at full size (2 x 4096 queries, text
+    keys 24 and 700 of capacity 4096, 32 / 8 heads, d 128): few 64-key
+    tiles, so the dK / dV loop of every tile is split into chunks whose FP32
+    partials a reduce pass sums.  Every used row and key against the
+    oracle; pad keys keep their sentinel."""
+    wl = W.config2()
+    check_case(wl, 990, "bwd cross-attention split")
