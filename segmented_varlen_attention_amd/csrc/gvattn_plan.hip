@@ -7,16 +7,19 @@
 //      an invalid segment gets no tiles and sets a device error bit; in the
 //      key-range form it also sums the segment's range lengths (its key
 //      count) into the workspace;
-//   2. prefix-sums the counts into per-segment tile offsets;
 //   2. when the launch has few query tiles, splits long key ranges into
 //      chunks (split-K: up to the workspace's capacity, chunks of at least
-//      kMinSplitTiles key tiles) and prefix-sums the work entries;
+//      kMinSplitTiles key tiles) and prefix-sums the work entries into
+//      per-segment offsets;
 //   3. histograms the entries by cost = number of key tiles they cover
 //      (under bottom-right causal the last row of a tile sees the most);
 //   4. scatters the entries into cost-descending order, so the persistent
 //      forward kernel starts the longest work first.
 // The order inside one cost bucket depends on atomics, but each tile's
 // result does not depend on the order, so outputs are deterministic.
+// Segment lengths, splits and offsets stay in LDS for launches of up to
+// kPlanLdsSegs segments (the tile loops then read no global memory), and the
+// prefix sums are wave shuffles plus one exchange of wave totals.
 #include "gvattn_internal.h"
 
 namespace gvattn {
@@ -24,21 +27,35 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 
+constexpr int kPlanWaves = kPlanThreads / 64;
+// Segments whose lengths, splits and entry offsets the plan keeps in LDS;
+// a launch with more segments reads them from global memory instead.
+constexpr int kPlanLdsSegs = 2048;
+
+// Exclusive prefix sum over the workgroup: an inclusive scan inside each
+// wave (shuffles), then the wave totals from LDS.  *total gets the sum of
+// all x.  `wsum` holds kPlanWaves values.
 template <typename T>
-__device__ T block_exclusive_scan(T x, T* tmp, T* total) {
-  const int t = threadIdx.x;
-  tmp[t] = x;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const T y = (t >= off) ? tmp[t - off] : T(0);
-    __syncthreads();
-    tmp[t] += y;
-    __syncthreads();
+__device__ T block_exclusive_scan(T x, T* wsum, T* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  T v = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
   }
-  const T incl = tmp[t];
-  *total = tmp[kPlanThreads - 1];
+  if (lane == 63) wsum[w] = v;
   __syncthreads();
-  return incl - x;
+  T base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) {
+    const T t = wsum[i];
+    base += (i < w) ? t : T(0);
+    tot += t;
+  }
+  *total = tot;
+  __syncthreads();  // wsum is reused by the next scan
+  return base + v - x;
 }
 
 // Key-range form: checks segment s's ranges and returns their total length
@@ -85,27 +102,31 @@ __device__ int segment_error(const PlanArgs& a, int s) {
   return err;
 }
 
-// Largest s with seg_off[s] <= t (t < seg_off[nseg]).
-__device__ int find_segment(const int32_t* seg_off, int nseg, int t) {
+// Per-segment values the tile loops read: in LDS when the launch has at most
+// kPlanLdsSegs segments, else the workspace / argument arrays.
+struct SegView {
+  const int32_t* uq;   // used query rows
+  const int32_t* uk;   // key count (0 for a segment the plan rejected)
+  int32_t* split;      // key chunks per query tile (query tiles until step 2)
+  int32_t* off;        // first entry of each segment, [nseg + 1]
+};
+
+// Largest s with off[s] <= t (t < off[nseg]).
+__device__ int find_segment(const int32_t* off, int nseg, int t) {
   int lo = 0, hi = nseg;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (seg_off[mid] <= t) lo = mid;
+    if (off[mid] <= t) lo = mid;
     else hi = mid - 1;
   }
   return lo;
 }
 
-// Key count of segment s (0 for a segment the plan rejected).
-__device__ int seg_key_count(const PlanArgs& a, int s) {
-  return (a.g.kr_off != nullptr) ? a.ws.seg_keys[s] : a.g.used_k[s];
-}
-
 // Key tiles the query tile at row0 of segment s sees (under bottom-right
 // causal its last row sees the most).
-__device__ int tile_key_tiles(const PlanArgs& a, int s, int row0) {
-  const int uq = a.g.used_q[s];
-  const int uk = seg_key_count(a, s);
+__device__ int tile_key_tiles(const PlanArgs& a, const SegView& v, int s, int row0) {
+  const int uq = v.uq[s];
+  const int uk = v.uk[s];
   int kend = uk;
   if (a.g.causal) {
     const int r_last = min(row0 + a.rows, uq) - 1;
@@ -115,19 +136,18 @@ __device__ int tile_key_tiles(const PlanArgs& a, int s, int row0) {
 }
 
 // Work entry e (its segment s, first entry of s at e0): query tile
-// (e - e0) / S and key chunk (e - e0) % S of the segment's S = seg_split[s]
+// (e - e0) / S and key chunk (e - e0) % S of the segment's S = split[s]
 // chunks; the chunk covers key tiles [kt0, kt1) of that query tile.
-__device__ int4 make_entry(const PlanArgs& a, int s, int e0, int e, int* cost) {
+__device__ int4 make_entry(const PlanArgs& a, const SegView& v, int s, int e0, int e, int* cost) {
+  const int S = v.split[s];
+  const int local = e - e0;
   if (a.mode == 1) {
     // key tile of `rows` keys: the query rows that see any of its keys
     // start at r_first (bottom-right causal); its loop runs over (query
-    // head, 32-row query tile), split into S chunks when the segment's
-    // seg_split S > 1 (chunk j of key tile kt is entry e0 + kt * S + j, and
-    // e names its partial slot)
-    const int S = a.ws.seg_split[s];
-    const int local = e - e0;
+    // head, 32-row query tile), split into S chunks when S > 1 (chunk j of
+    // key tile kt is entry e0 + kt * S + j, and e names its partial slot)
     const int kt = local / S, j = local - kt * S;
-    const int uq = a.g.used_q[s], uk = seg_key_count(a, s);
+    const int uq = v.uq[s], uk = v.uk[s];
     const int k_row0 = kt * a.rows;
     const int r_first = a.g.causal ? max(0, min(uq, k_row0 + uq - uk)) : 0;
     const int n_it = (a.g.hq / a.g.hkv) * ((uq + 31) / 32 - r_first / 32);
@@ -140,11 +160,9 @@ __device__ int4 make_entry(const PlanArgs& a, int s, int e0, int e, int* cost) {
     *cost = min(it1 - it0, kCostBuckets - 1);
     return make_int4(s, k_row0, r_first, (e << 5) | (j << 1) | (S > 1 ? 1 : 0));
   }
-  const int S = a.ws.seg_split[s];
-  const int local = e - e0;
   const int qt = local / S, j = local - qt * S;
   const int row0 = qt * a.rows;
-  const int nkt = tile_key_tiles(a, s, row0);
+  const int nkt = tile_key_tiles(a, v, s, row0);
   const int chunk = (nkt + S - 1) / S;
   const int kt0 = min(j * chunk, nkt);
   const int kt1 = min(kt0 + chunk, nkt);
@@ -153,14 +171,21 @@ __device__ int4 make_entry(const PlanArgs& a, int s, int e0, int e, int* cost) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ long long tmp64[kPlanThreads];
-  __shared__ int tmp[kPlanThreads];
+  __shared__ long long wsum64[kPlanWaves];
+  __shared__ int wsum[kPlanWaves];
   __shared__ int hist[kCostBuckets];
+  __shared__ int32_t l_uq[kPlanLdsSegs], l_uk[kPlanLdsSegs], l_split[kPlanLdsSegs];
+  __shared__ int32_t l_off[kPlanLdsSegs + 1];
   __shared__ int s_err;
   __shared__ int s_max_split;
   const int tid = threadIdx.x;
   const int nseg = a.g.nseg;
-  int32_t* seg_off = a.ws.seg_tile_off;
+  const bool in_lds = nseg <= kPlanLdsSegs;
+  SegView v;
+  v.uq = in_lds ? l_uq : a.g.used_q;
+  v.uk = in_lds ? l_uk : (a.g.kr_off != nullptr ? a.ws.seg_keys : a.g.used_k);
+  v.split = in_lds ? l_split : a.ws.seg_split;
+  v.off = in_lds ? l_off : a.ws.seg_tile_off;
 
   for (int b = tid; b < kCostBuckets; b += kPlanThreads) hist[b] = 0;
   if (tid == 0) {
@@ -170,19 +195,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __syncthreads();
 
   // 1. validation and query tiles per segment (an invalid segment: none).
-  //    seg_split holds the segment's query-tile count until step 2.
+  //    split holds the segment's tile count until step 2.
   long long n_qtiles = 0;
   for (int base = 0; base < nseg; base += kPlanThreads) {
     const int s = base + tid;
     long long cnt = 0;
     if (s < nseg) {
       const int err = segment_error(a, s);
+      const int uq = a.g.used_q[s];
+      const int uk = err ? 0 : (a.g.kr_off != nullptr ? a.ws.seg_keys[s] : a.g.used_k[s]);
       if (err) atomicOr(&s_err, err);
-      else cnt = ((a.mode == 1 ? seg_key_count(a, s) : a.g.used_q[s]) + a.rows - 1) / a.rows;
-      a.ws.seg_split[s] = (int32_t)cnt;
+      else cnt = ((a.mode == 1 ? uk : uq) + a.rows - 1) / a.rows;
+      if (in_lds) {
+        l_uq[s] = uq;
+        l_uk[s] = uk;
+      }
+      v.split[s] = (int32_t)cnt;
     }
     long long tot;
-    block_exclusive_scan<long long>(cnt, tmp64, &tot);
+    block_exclusive_scan<long long>(cnt, wsum64, &tot);
     n_qtiles += tot;
   }
   __threadfence_block();
@@ -209,24 +240,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int s = base + tid;
     long long cnt = 0;
     if (s < nseg) {
-      const int qt = a.ws.seg_split[s];
+      const int qt = v.split[s];
       int S = 1;
       if (split_on && qt > 0) {
         if (a.mode == 0) {
-          const int kt = (seg_key_count(a, s) + a.key_tile - 1) / a.key_tile;
+          const int kt = (v.uk[s] + a.key_tile - 1) / a.key_tile;
           S = max(1, min(s_aim, kt / kMinSplitTiles));
         } else {  // chunks of at least kBwdMinChunk (head, query tile) steps
-          const int steps = (a.g.hq / a.g.hkv) * ((a.g.used_q[s] + 31) / 32);
+          const int steps = (a.g.hq / a.g.hkv) * ((v.uq[s] + 31) / 32);
           S = max(1, min(s_aim, steps / kBwdMinChunk));
         }
       }
-      a.ws.seg_split[s] = S;
+      v.split[s] = S;
       if (S > 1) atomicMax(&s_max_split, S);
       cnt = (long long)qt * S;
     }
     long long tot;
-    const long long excl = block_exclusive_scan<long long>(cnt, tmp64, &tot);
-    if (s < nseg) seg_off[s] = (int32_t)min(carry + excl, cap);
+    const long long excl = block_exclusive_scan<long long>(cnt, wsum64, &tot);
+    if (s < nseg) v.off[s] = (int32_t)min(carry + excl, cap);
     carry += tot;
   }
   int n_tiles = (int)min(carry, cap);
@@ -234,15 +265,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     n_tiles = 0;
     if (tid == 0) s_err |= GVATTN_DEVERR_OFFSETS;
   }
-  if (tid == 0) seg_off[nseg] = n_tiles;
+  if (tid == 0) v.off[nseg] = n_tiles;
   __threadfence_block();
   __syncthreads();
 
   // 3. cost histogram
   for (int t = tid; t < n_tiles; t += kPlanThreads) {
-    const int s = find_segment(seg_off, nseg, t);
+    const int s = find_segment(v.off, nseg, t);
     int cost;
-    make_entry(a, s, seg_off[s], t, &cost);
+    make_entry(a, v, s, v.off[s], t, &cost);
     atomicAdd(&hist[cost], 1);
   }
   __syncthreads();
@@ -253,18 +284,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int b_lo = b_hi - 1;
   const int c_hi = hist[b_hi], c_lo = hist[b_lo];
   int tot;
-  const int excl = block_exclusive_scan<int>(c_hi + c_lo, tmp, &tot);
+  const int excl = block_exclusive_scan<int>(c_hi + c_lo, wsum, &tot);
   hist[b_hi] = excl;
   hist[b_lo] = excl + c_hi;
   __syncthreads();
 
   // 4. scatter
   for (int t = tid; t < n_tiles; t += kPlanThreads) {
-    const int s = find_segment(seg_off, nseg, t);
+    const int s = find_segment(v.off, nseg, t);
     int cost;
-    const int4 e = make_entry(a, s, seg_off[s], t, &cost);
+    const int4 e = make_entry(a, v, s, v.off[s], t, &cost);
     const int pos = atomicAdd(&hist[cost], 1);
     a.ws.tiles[pos] = e;
+  }
+
+  // the kernels read seg_split (and seg_keys, written in step 1)
+  if (in_lds) {
+    for (int s = tid; s < nseg; s += kPlanThreads) {
+      a.ws.seg_split[s] = l_split[s];
+      a.ws.seg_tile_off[s] = l_off[s];
+    }
+    if (tid == 0) a.ws.seg_tile_off[nseg] = l_off[nseg];
   }
   __syncthreads();
 

@@ -164,6 +164,20 @@ def test_bwd_ragged_edges():
     check_case(wl, 961, "bwd ragged noncausal")
 
 
+@pytest.mark.parametrize("nseg", [600, 2500])
+def test_bwd_many_segments(nseg):
+    """Many short segments (capacity <= 40): with 2500 the plans read the
+    segment table from global memory instead of LDS."""
+    seed = 980 + nseg
+    rng = np.random.default_rng(seed)
+    cq, ck = rng.integers(0, 41, nseg), rng.integers(0, 41, nseg)
+    uq = np.array([rng.integers(0, c + 1) for c in cq])
+    uk = np.array([rng.integers(0, c + 1) for c in ck])
+    g = W.make_geometry(cq, ck, uq, uk, 4, 2, 64, causal=True)
+    q, k, v = W.fill_qkv(g, seed)
+    check_case(W.Workload(f"bwd_many_{nseg}", seed, g, q, k, v), seed, f"bwd many {nseg}")
+
+
 def test_bwd_deterministic():
     wl = W.random_small(970, 4, 100, 150, 8, 2, 128, True, W.BF16)
     q, k, v, o, l, do, _, _ = make_inputs(wl, 970)

@@ -92,10 +92,12 @@ def test_small_fp32(d, causal):
     say("   ", compare_full(out, lse, wl, where=f"fp32 d{d} c{int(causal)}"))
 
 
-def test_many_segments_tiny_lengths():
-    """1000 segments of capacity <= 5: many empty and one-row tiles."""
-    rng = np.random.default_rng(7)
-    nseg = 1000
+@pytest.mark.parametrize("nseg", [1000, 3000])
+def test_many_segments_tiny_lengths(nseg):
+    """Segments of capacity <= 5: many empty and one-row tiles.  The plan
+    keeps up to 2048 segments in LDS and reads more from global memory, so
+    the two counts take both paths."""
+    rng = np.random.default_rng(7 + nseg)
     caps_q = rng.integers(0, 6, nseg)
     caps_k = rng.integers(0, 6, nseg)
     uq = np.array([rng.integers(0, c + 1) for c in caps_q])
@@ -104,7 +106,8 @@ def test_many_segments_tiny_lengths():
     q, k, v = W.fill_qkv(g, 8)
     wl = W.Workload("tiny_many", 7, g, q, k, v)
     out, lse, _ = DeviceCase(wl).fwd()
-    say("[many tiny]", compare_full(out, lse, wl, where="many tiny", derived=True))
+    say(f"[many tiny {nseg}]", compare_full(out, lse, wl, where=f"many tiny {nseg}",
+                                            derived=True))
 
 
 # --- the five workloads -------------------------------------------------------------
