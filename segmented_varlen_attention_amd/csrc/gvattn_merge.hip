@@ -8,7 +8,9 @@
 //        O = sum_p (w_p / W) O_p.
 // The kernel is HBM-bound: D/32 lanes own one (row, head), 32 elements each,
 // moved with 16-byte vector loads/stores; the per-row work (segment lookup,
-// LSE loads, weights) is shared by few lanes.  Pairs are taken in row-major
+// LSE loads, weights) is shared by few lanes.  With two partials (the
+// common case) every load of the lane is issued before the dependent
+// segment and LSE reads.  Pairs are taken in row-major
 // order (all heads of a row, then the next row), which is the memory order
 // of O, so a block streams one contiguous piece of every partial and of the
 // output.
@@ -26,14 +28,16 @@ using namespace dev;
 constexpr int kThreads = 256;
 constexpr int kElems = 32;  // elements of one (row, head) per lane
 
+// 8 elements of type T: 16-byte loads into raw registers, unpacking to
+// FP32, and packing / storing FP32 back as T (round to nearest even).
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> {
-  static __device__ __forceinline__ void load(const void* p, float* f) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  static constexpr int kRaw = 1;  // 16-byte registers per 8 elements
+  static __device__ __forceinline__ void unpack(const u32x4* r, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __builtin_bit_cast(float, v[i] << 16);
-      f[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+      f[2 * i] = __builtin_bit_cast(float, r[0][i] << 16);
+      f[2 * i + 1] = __builtin_bit_cast(float, r[0][i] & 0xffff0000u);
     }
   }
   static __device__ __forceinline__ void store(void* p, const float* f) {
@@ -45,8 +49,9 @@ template <> struct Vec8<__bf16> {
 };
 template <> struct Vec8<_Float16> {
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  static __device__ __forceinline__ void load(const void* p, float* f) {
-    const f16x8 v = *reinterpret_cast<const f16x8*>(p);
+  static constexpr int kRaw = 1;
+  static __device__ __forceinline__ void unpack(const u32x4* r, float* f) {
+    const f16x8 v = __builtin_bit_cast(f16x8, r[0]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
   }
@@ -58,9 +63,12 @@ template <> struct Vec8<_Float16> {
   }
 };
 template <> struct Vec8<float> {
-  static __device__ __forceinline__ void load(const void* p, float* f) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-    const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+  static constexpr int kRaw = 2;
+  static __device__ __forceinline__ void unpack(const u32x4* r, float* f) {
+    // whole-vector casts: a bit cast of one element of a vector lvalue
+    // (r[0][i]) compiles to a read of element 0
+    const f32x4 a = __builtin_bit_cast(f32x4, r[0]);
+    const f32x4 b = __builtin_bit_cast(f32x4, r[1]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[i] = a[i];
@@ -79,6 +87,21 @@ template <> struct Vec8<float> {
   }
 };
 
+// The kElems elements of one lane as raw 16-byte registers.
+template <typename T>
+struct LaneRaw {
+  static constexpr int N = kElems / 8 * Vec8<T>::kRaw;
+  u32x4 r[N];
+  __device__ __forceinline__ void load(const T* src) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i] = reinterpret_cast<const u32x4*>(src)[i];
+  }
+  __device__ __forceinline__ void unpack(float* f) const {
+#pragma unroll
+    for (int c = 0; c < kElems / 8; ++c) Vec8<T>::unpack(r + c * Vec8<T>::kRaw, f + 8 * c);
+  }
+};
+
 // Largest s in [0, nseg) with cu[s] <= row (cu assumed non-decreasing;
 // callers re-check membership).
 __device__ __forceinline__ int find_segment(const int32_t* cu, int nseg, int row) {
@@ -91,7 +114,95 @@ __device__ __forceinline__ int find_segment(const int32_t* cu, int nseg, int row
   return lo;
 }
 
-template <typename TIn, typename TOut, int D>
+// Merges the pair first + slot (its D/32 lanes; this lane holds part `sub`).
+// NP > 0: exactly NP partials, whose loads are all issued before the row's
+// segment and LSEs are looked up, so that they overlap those dependent
+// reads; NP == 0: any count, one partial at a time.
+template <typename TIn, typename TOut, int D, int NP>
+__device__ __forceinline__ void merge_pair(const MergeArgs& a, int64_t first, int slot, int sub,
+                                            int64_t npairs) {
+  if (first + slot >= npairs) return;
+  const int64_t row_first = first / a.hq;  // uniform
+  const int t = (int)(first - row_first * a.hq) + slot;
+  const int row = (int)(row_first + t / a.hq);
+  const int head = t % a.hq;
+  const int64_t eoff = ((int64_t)row * a.hq + head) * D + sub * kElems;
+
+  // row < total_q: every partial holds the row, used or not
+  LaneRaw<TIn> raw[NP > 0 ? NP : 1];
+  if constexpr (NP > 0) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) raw[p].load(static_cast<const TIn*>(a.part_out[p]) + eoff);
+  }
+  {
+    const int s = find_segment(a.cu_q, a.nseg, row);
+    const int c0 = a.cu_q[s], c1 = a.cu_q[s + 1], us = a.used_q[s];
+    if (c0 < 0 || c1 < c0 || c1 > a.total_q || us < 0 || us > c1 - c0) return;
+    if (row < c0 || row >= c0 + us) return;  // gap row: untouched
+  }
+
+  const int64_t lidx = (int64_t)head * a.total_q + row;
+  const int np = NP > 0 ? NP : a.nparts;
+  float lp[NP > 0 ? NP : 1];
+  float m = -INFINITY;
+  bool nan = false;
+  if constexpr (NP > 0) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) lp[p] = a.part_lse[p][lidx];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      nan |= (lp[p] != lp[p]);
+      m = fmaxf(m, lp[p]);
+    }
+  } else {
+    for (int p = 0; p < np; ++p) {
+      const float L = a.part_lse[p][lidx];
+      nan |= (L != L);
+      m = fmaxf(m, L);
+    }
+  }
+  float acc[kElems];
+#pragma unroll
+  for (int i = 0; i < kElems; ++i) acc[i] = 0.f;
+  float lse_out;
+  if (nan) {
+#pragma unroll
+    for (int i = 0; i < kElems; ++i) acc[i] = NAN;
+    lse_out = NAN;
+  } else if (m == -INFINITY) {
+    lse_out = -INFINITY;
+  } else {
+    constexpr float kLog2e = 1.4426950408889634f;
+    float wsum = 0.f;
+    auto add = [&](float L, const LaneRaw<TIn>& r) {
+      const float w = __builtin_amdgcn_exp2f((L - m) * kLog2e);
+      float f[kElems];
+      r.unpack(f);
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < kElems; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
+    };
+    if constexpr (NP > 0) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) add(lp[p], raw[p]);
+    } else {
+      for (int p = 0; p < np; ++p) {
+        raw[0].load(static_cast<const TIn*>(a.part_out[p]) + eoff);
+        add(a.part_lse[p][lidx], raw[0]);
+      }
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int i = 0; i < kElems; ++i) acc[i] *= inv;
+    lse_out = m + logf(wsum);
+  }
+  TOut* dst = static_cast<TOut*>(a.out) + eoff;
+#pragma unroll
+  for (int c = 0; c < kElems / 8; ++c) Vec8<TOut>::store(dst + 8 * c, acc + 8 * c);
+  if (sub == 0) a.lse[lidx] = lse_out;
+}
+
+template <typename TIn, typename TOut, int D, int NP>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   constexpr int LPP = D / kElems;          // lanes per (row, head)
   constexpr int PPB = kThreads / LPP;      // pairs per block
@@ -111,82 +222,33 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   }
 
   // pair = row * hq + head: the block's pairs are contiguous in O
-  const int64_t first = (int64_t)blockIdx.x * PPB;
-  if (first + slot >= npairs) return;
-  const int64_t row_first = first / a.hq;  // uniform
-  const int t = (int)(first - row_first * a.hq) + slot;
-  const int row = (int)(row_first + t / a.hq);
-  const int head = t % a.hq;
-  {
-    const int s = find_segment(a.cu_q, a.nseg, row);
-    const int c0 = a.cu_q[s], c1 = a.cu_q[s + 1], us = a.used_q[s];
-    if (c0 < 0 || c1 < c0 || c1 > a.total_q || us < 0 || us > c1 - c0) return;
-    if (row < c0 || row >= c0 + us) return;  // gap row: untouched
-  }
+  merge_pair<TIn, TOut, D, NP>(a, (int64_t)blockIdx.x * PPB, slot, sub, npairs);
+}
 
-  const int64_t lidx = (int64_t)head * a.total_q + row;
-  float m = -INFINITY;
-  bool nan = false;
-  for (int p = 0; p < a.nparts; ++p) {
-    const float L = a.part_lse[p][lidx];
-    nan |= (L != L);
-    m = fmaxf(m, L);
-  }
-  const int64_t eoff = ((int64_t)row * a.hq + head) * D + sub * kElems;
-  float acc[kElems];
-#pragma unroll
-  for (int i = 0; i < kElems; ++i) acc[i] = 0.f;
-  float lse_out;
-  if (nan) {
-#pragma unroll
-    for (int i = 0; i < kElems; ++i) acc[i] = NAN;
-    lse_out = NAN;
-  } else if (m == -INFINITY) {
-    lse_out = -INFINITY;
-  } else {
-    constexpr float kLog2e = 1.4426950408889634f;
-    float wsum = 0.f;
-    for (int p = 0; p < a.nparts; ++p) {
-      const float w = __builtin_amdgcn_exp2f((a.part_lse[p][lidx] - m) * kLog2e);
-      const TIn* src = static_cast<const TIn*>(a.part_out[p]) + eoff;
-      float f[kElems];
-#pragma unroll
-      for (int c = 0; c < kElems / 8; ++c) Vec8<TIn>::load(src + 8 * c, f + 8 * c);
-      wsum += w;
-#pragma unroll
-      for (int i = 0; i < kElems; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
-    }
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int i = 0; i < kElems; ++i) acc[i] *= inv;
-    lse_out = m + logf(wsum);
-  }
-  TOut* dst = static_cast<TOut*>(a.out) + eoff;
-#pragma unroll
-  for (int c = 0; c < kElems / 8; ++c) Vec8<TOut>::store(dst + 8 * c, acc + 8 * c);
-  if (sub == 0) a.lse[lidx] = lse_out;
+template <typename TIn, typename TOut, int D>
+void launch_np(const MergeArgs& a, int grid, hipStream_t s) {
+  if (a.nparts == 2)
+    hipLaunchKernelGGL((merge_kernel<TIn, TOut, D, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<TIn, TOut, D, 0>), dim3(grid), dim3(kThreads), 0, s, a);
 }
 
 template <typename TIn, typename TOut>
 hipError_t launch_t(const MergeArgs& a, hipStream_t s, bool* ok) {
-  const void* k = nullptr;
-  switch (a.d) {
-    case 64: k = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, 64>); break;
-    case 128: k = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, 128>); break;
-    case 256: k = reinterpret_cast<const void*>(merge_kernel<TIn, TOut, 256>); break;
-    default: *ok = false; return hipSuccess;
+  if (a.d != 64 && a.d != 128 && a.d != 256) {
+    *ok = false;
+    return hipSuccess;
   }
   *ok = true;
-  (void)k;
   const int per_block = kThreads / (a.d / kElems);
   const int64_t blocks = ((int64_t)a.hq * a.total_q + per_block - 1) / per_block;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int grid = (int)blocks;
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((merge_kernel<TIn, TOut, 64>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((merge_kernel<TIn, TOut, 128>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((merge_kernel<TIn, TOut, 256>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 64: launch_np<TIn, TOut, 64>(a, grid, s); break;
+    case 128: launch_np<TIn, TOut, 128>(a, grid, s); break;
+    default: launch_np<TIn, TOut, 256>(a, grid, s); break;
   }
   return hipGetLastError();
 }
@@ -230,9 +292,10 @@ __global__ __launch_bounds__(kThreads) void split_merge_kernel(FwdArgs a) {
       const float L = a.ws.part_lse[((int64_t)j * hq + head) * total_q + row];
       const float w = __builtin_amdgcn_exp2f((L - m) * kLog2e);
       const float* src = a.ws.part_o + (((int64_t)j * total_q + row) * hq + head) * D + sub * kElems;
+      LaneRaw<float> r;
+      r.load(src);
       float f[kElems];
-#pragma unroll
-      for (int c = 0; c < kElems / 8; ++c) Vec8<float>::load(src + 8 * c, f + 8 * c);
+      r.unpack(f);
       wsum += w;
 #pragma unroll
       for (int i = 0; i < kElems; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);

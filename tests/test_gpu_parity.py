@@ -296,10 +296,11 @@ def test_device_errors_skip_bad_segments():
     assert B.gvattn_read_device_error(ws) & B.GVATTN_DEVERR_OFFSETS
 
 
+@pytest.mark.parametrize("nparts", [2, 3])
 @pytest.mark.parametrize("pdt,odt", [("bf16", "bf16"), ("fp32", "fp32"), ("fp32", "bf16"),
                                      ("fp16", "fp16"), ("fp16", "fp32"), ("bf16", "fp16")])
-def test_merge_small(pdt, odt):
-    """Three key partitions (one of them empty for some segments) merged on
+def test_merge_small(pdt, odt, nparts):
+    """Two or three key partitions (some empty for some segments) merged on
     the device.  The merge kernel itself is held to FP32 accuracy against
     the oracle merge of the very partials it was given; end to end, the
     merged result matches the single-pass oracle within the derived bound of
@@ -313,10 +314,10 @@ def test_merge_small(pdt, odt):
     g = wl.geom
     dc = DeviceCase(wl)
     cuts = []
-    for frac in (0.0, 0.3, 0.7, 1.0):
+    for frac in ((0.0, 0.3, 0.7, 1.0) if nparts == 3 else (0.0, 0.45, 1.0)):
         cuts.append([int(round(frac * u)) for u in g.used_k])
     outs, lses = [], []
-    for p in range(3):
+    for p in range(nparts):
         cu = np.array([g.cu_k[s] + cuts[p][s] for s in range(g.nseg)] + [g.total_k], np.int32)
         used = np.array([cuts[p + 1][s] - cuts[p][s] for s in range(g.nseg)], np.int32)
         o, l, _ = dc.fwd(g.with_keys(cu, used))
@@ -337,8 +338,8 @@ def test_merge_small(pdt, odt):
     m = used_row_mask(g)
     o_gpu, l_gpu = to_np(out), to_np(lse)
     st = compare(o_gpu[m], l_gpu[:, m], om_ref[m], lm_ref[:, m], odt,
-                 f"merge kernel {pdt}->{odt}", tol_out=1e-5)
-    say(f"[merge kernel {pdt}->{odt}]", st)
+                 f"merge kernel {pdt}->{odt} x{nparts}", tol_out=1e-5)
+    say(f"[merge kernel {pdt}->{odt} x{nparts}]", st)
     o_abs = oracle_abs(wl)[m]
     st2 = compare(o_gpu[m], l_gpu[:, m], o_ref[m], l_ref[:, m], fw,
                   f"merge end-to-end {pdt}->{odt}", o_abs=2 * o_abs)
