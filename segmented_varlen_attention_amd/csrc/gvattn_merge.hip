@@ -26,7 +26,11 @@ namespace {
 using namespace dev;
 
 constexpr int kThreads = 256;
-constexpr int kElems = 32;  // elements of one (row, head) per lane
+constexpr int kElems = 32;  // split merge: elements of one (row, head) per lane
+// LSE merge: elements of one (row, head) per lane, held in runs of 8 spread
+// over the row so that each 16-byte load instruction of the D/kMergeElems
+// lanes of a pair reads one contiguous piece of it
+constexpr int kMergeElems = 16;
 
 // 8 elements of type T: 16-byte loads into raw registers, unpacking to
 // FP32, and packing / storing FP32 back as T (round to nearest even).
@@ -87,20 +91,30 @@ template <> struct Vec8<float> {
   }
 };
 
-// The kElems elements of one lane as raw 16-byte registers.
-template <typename T>
+// E elements of one lane, in runs of 8 contiguous elements STRIDE elements
+// apart, as raw 16-byte registers; and the store of such runs.
+template <typename T, int E, int STRIDE>
 struct LaneRaw {
-  static constexpr int N = kElems / 8 * Vec8<T>::kRaw;
-  u32x4 r[N];
+  static constexpr int RUNS = E / 8;
+  static constexpr int K = Vec8<T>::kRaw;
+  u32x4 r[RUNS * K];
   __device__ __forceinline__ void load(const T* src) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) r[i] = reinterpret_cast<const u32x4*>(src)[i];
+    for (int j = 0; j < RUNS; ++j)
+#pragma unroll
+      for (int k = 0; k < K; ++k) r[j * K + k] = reinterpret_cast<const u32x4*>(src + j * STRIDE)[k];
   }
   __device__ __forceinline__ void unpack(float* f) const {
 #pragma unroll
-    for (int c = 0; c < kElems / 8; ++c) Vec8<T>::unpack(r + c * Vec8<T>::kRaw, f + 8 * c);
+    for (int j = 0; j < RUNS; ++j) Vec8<T>::unpack(r + j * K, f + 8 * j);
   }
 };
+
+template <typename T, int E, int STRIDE>
+__device__ __forceinline__ void store_runs(T* dst, const float* f) {
+#pragma unroll
+  for (int j = 0; j < E / 8; ++j) Vec8<T>::store(dst + j * STRIDE, f + 8 * j);
+}
 
 // Largest s in [0, nseg) with cu[s] <= row (cu assumed non-decreasing;
 // callers re-check membership).
@@ -126,10 +140,11 @@ __device__ __forceinline__ void merge_pair(const MergeArgs& a, int64_t first, in
   const int t = (int)(first - row_first * a.hq) + slot;
   const int row = (int)(row_first + t / a.hq);
   const int head = t % a.hq;
-  const int64_t eoff = ((int64_t)row * a.hq + head) * D + sub * kElems;
+  constexpr int E = kMergeElems, RS = D * 8 / E;  // run stride
+  const int64_t eoff = ((int64_t)row * a.hq + head) * D + sub * 8;
 
   // row < total_q: every partial holds the row, used or not
-  LaneRaw<TIn> raw[NP > 0 ? NP : 1];
+  LaneRaw<TIn, E, RS> raw[NP > 0 ? NP : 1];
   if constexpr (NP > 0) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) raw[p].load(static_cast<const TIn*>(a.part_out[p]) + eoff);
@@ -161,26 +176,26 @@ __device__ __forceinline__ void merge_pair(const MergeArgs& a, int64_t first, in
       m = fmaxf(m, L);
     }
   }
-  float acc[kElems];
+  float acc[E];
 #pragma unroll
-  for (int i = 0; i < kElems; ++i) acc[i] = 0.f;
+  for (int i = 0; i < E; ++i) acc[i] = 0.f;
   float lse_out;
   if (nan) {
 #pragma unroll
-    for (int i = 0; i < kElems; ++i) acc[i] = NAN;
+    for (int i = 0; i < E; ++i) acc[i] = NAN;
     lse_out = NAN;
   } else if (m == -INFINITY) {
     lse_out = -INFINITY;
   } else {
     constexpr float kLog2e = 1.4426950408889634f;
     float wsum = 0.f;
-    auto add = [&](float L, const LaneRaw<TIn>& r) {
+    auto add = [&](float L, const LaneRaw<TIn, E, RS>& r) {
       const float w = __builtin_amdgcn_exp2f((L - m) * kLog2e);
-      float f[kElems];
+      float f[E];
       r.unpack(f);
       wsum += w;
 #pragma unroll
-      for (int i = 0; i < kElems; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
+      for (int i = 0; i < E; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
     };
     if constexpr (NP > 0) {
 #pragma unroll
@@ -193,18 +208,16 @@ __device__ __forceinline__ void merge_pair(const MergeArgs& a, int64_t first, in
     }
     const float inv = 1.f / wsum;
 #pragma unroll
-    for (int i = 0; i < kElems; ++i) acc[i] *= inv;
+    for (int i = 0; i < E; ++i) acc[i] *= inv;
     lse_out = m + logf(wsum);
   }
-  TOut* dst = static_cast<TOut*>(a.out) + eoff;
-#pragma unroll
-  for (int c = 0; c < kElems / 8; ++c) Vec8<TOut>::store(dst + 8 * c, acc + 8 * c);
+  store_runs<TOut, E, RS>(static_cast<TOut*>(a.out) + eoff, acc);
   if (sub == 0) a.lse[lidx] = lse_out;
 }
 
 template <typename TIn, typename TOut, int D, int NP>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  constexpr int LPP = D / kElems;          // lanes per (row, head)
+  constexpr int LPP = D / kMergeElems;     // lanes per (row, head)
   constexpr int PPB = kThreads / LPP;      // pairs per block
   const int sub = threadIdx.x % LPP;
   const int slot = threadIdx.x / LPP;
@@ -240,7 +253,7 @@ hipError_t launch_t(const MergeArgs& a, hipStream_t s, bool* ok) {
     return hipSuccess;
   }
   *ok = true;
-  const int per_block = kThreads / (a.d / kElems);
+  const int per_block = kThreads / (a.d / kMergeElems);
   const int64_t blocks = ((int64_t)a.hq * a.total_q + per_block - 1) / per_block;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -292,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void split_merge_kernel(FwdArgs a) {
       const float L = a.ws.part_lse[((int64_t)j * hq + head) * total_q + row];
       const float w = __builtin_amdgcn_exp2f((L - m) * kLog2e);
       const float* src = a.ws.part_o + (((int64_t)j * total_q + row) * hq + head) * D + sub * kElems;
-      LaneRaw<float> r;
+      LaneRaw<float, kElems, 8> r;
       r.load(src);
       float f[kElems];
       r.unpack(f);
@@ -305,9 +318,8 @@ __global__ __launch_bounds__(kThreads) void split_merge_kernel(FwdArgs a) {
     for (int i = 0; i < kElems; ++i) acc[i] *= inv;
     lse_out = m + logf(wsum);
   }
-  TOut* dst = static_cast<TOut*>(a.out) + ((int64_t)row * hq + head) * D + sub * kElems;
-#pragma unroll
-  for (int c = 0; c < kElems / 8; ++c) Vec8<TOut>::store(dst + 8 * c, acc + 8 * c);
+  store_runs<TOut, kElems, 8>(static_cast<TOut*>(a.out) + ((int64_t)row * hq + head) * D + sub * kElems,
+                              acc);
   if (sub == 0) a.lse[(int64_t)head * total_q + row] = lse_out;
 }
 
