@@ -41,8 +41,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# the translation unit of the attention forward kernel the counters cover
-FWD_SOURCES = ("gvattn_fwd_mfma.hip", "gvattn_mfma.h", "gvattn_internal.h")
+# the sources of the attention forward kernel and of the plan that orders
+# its work, which the counters cover
+FWD_SOURCES = ("gvattn_fwd_mfma.hip", "gvattn_plan.hip", "gvattn_mfma.h", "gvattn_internal.h")
 
 
 def kernel_source_hash() -> str:

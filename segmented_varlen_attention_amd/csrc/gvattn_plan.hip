@@ -28,6 +28,9 @@ namespace {
 constexpr int kPlanThreads = 1024;
 
 constexpr int kPlanWaves = kPlanThreads / 64;
+// Forward entries are ordered by cost in groups of 2^kGroupShift key tiles,
+// then by segment.
+constexpr int kGroupShift = 3;
 // Segments whose lengths, splits and entry offsets the plan keeps in LDS;
 // a launch with more segments reads them from global memory instead.
 constexpr int kPlanLdsSegs = 2048;
@@ -178,6 +181,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int32_t l_off[kPlanLdsSegs + 1];
   __shared__ int s_err;
   __shared__ int s_max_split;
+  __shared__ int s_max_kt;
   const int tid = threadIdx.x;
   const int nseg = a.g.nseg;
   const bool in_lds = nseg <= kPlanLdsSegs;
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (tid == 0) {
     s_err = 0;
     s_max_split = 1;
+    s_max_kt = 0;
   }
   __syncthreads();
 
@@ -206,6 +211,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int uk = err ? 0 : (a.g.kr_off != nullptr ? a.ws.seg_keys[s] : a.g.used_k[s]);
       if (err) atomicOr(&s_err, err);
       else cnt = ((a.mode == 1 ? uk : uq) + a.rows - 1) / a.rows;
+      if (!err && uq > 0) atomicMax(&s_max_kt, (uk + a.key_tile - 1) / a.key_tile);
       if (in_lds) {
         l_uq[s] = uq;
         l_uk[s] = uk;
@@ -269,12 +275,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __threadfence_block();
   __syncthreads();
 
-  // 3. cost histogram
+  // 3. histogram of the sort keys.  Forward entries sort by their cost
+  // coarsened to 2^kGroupShift key tiles, then by segment, when that key
+  // fits the buckets: the static schedule runs consecutive entries at the
+  // same time on one XCD, so grouping them by segment keeps fewer
+  // segments' K/V in its L2 while the order stays longest first to within
+  // the coarsening.  Otherwise (and for the key-tile plan) the key is the
+  // cost.
+  const bool grouped = a.mode == 0 &&
+                       ((long long)(min(s_max_kt, kCostBuckets - 1) >> kGroupShift) + 1) * nseg <=
+                           kCostBuckets;
+  auto sort_key = [&](int cost, int s) {
+    return grouped ? (cost >> kGroupShift) * nseg + (nseg - 1 - s) : cost;
+  };
   for (int t = tid; t < n_tiles; t += kPlanThreads) {
     const int s = find_segment(v.off, nseg, t);
     int cost;
     make_entry(a, v, s, v.off[s], t, &cost);
-    atomicAdd(&hist[cost], 1);
+    atomicAdd(&hist[sort_key(cost, s)], 1);
   }
   __syncthreads();
 
@@ -294,7 +312,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int s = find_segment(v.off, nseg, t);
     int cost;
     const int4 e = make_entry(a, v, s, v.off[s], t, &cost);
-    const int pos = atomicAdd(&hist[cost], 1);
+    const int pos = atomicAdd(&hist[sort_key(cost, s)], 1);
     a.ws.tiles[pos] = e;
   }
 
