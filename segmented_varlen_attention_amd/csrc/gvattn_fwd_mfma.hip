@@ -33,6 +33,8 @@
 //     masks set scores to -inf on boundary tiles only.
 #include <math.h>
 
+#include <type_traits>
+
 #include "gvattn_internal.h"
 #include "gvattn_mfma.h"
 
@@ -236,8 +238,10 @@ void fwd_mfma_kernel(FwdArgs a) {
     const auto kr = k_rsrc(kfirst, klen);
     const auto vr = v_rsrc(kfirst, klen);
 
+    // the first tile of the item goes to stage 0 (the stage of a tile is
+    // its parity counted from kt_begin, a compile-time constant below)
     auto issue_tile = [&](int kt) {
-      char* st = lds + (kt & 1) * C::STAGE_BYTES;
+      char* st = lds;
       const uint32_t soffk = (uint32_t)kt * C::BN * kstride;
       const uint32_t soffv = (uint32_t)kt * C::BN * vstride;
 #pragma unroll
@@ -273,10 +277,14 @@ void fwd_mfma_kernel(FwdArgs a) {
     const int lim_w = a.g.causal ? min(uk, wr0 + uk - uq + 1) : uk;  // wave minimum
 
     KeyCursor nx = cur;
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
+    // One tile: stage ST holds it, the loads of the next tile go to stage
+    // 1 - ST.  With the stage a constant (std::integral_constant) every LDS
+    // operand address is a per-lane register plus an immediate offset.
+    auto tile_step = [&](int kt, auto stage_c) __attribute__((always_inline)) {
+      const int ST = stage_c;
       wait_vmem();
       __syncthreads();
-      const char* Ks = lds + (kt & 1) * C::STAGE_BYTES;
+      const char* Ks = lds + ST * C::STAGE_BYTES;
       const char* Vs = Ks + C::K_TILE_BYTES;
       if constexpr (KR) advance(nx);
 
@@ -288,7 +296,7 @@ void fwd_mfma_kernel(FwdArgs a) {
       const int nfirst = KR ? nx.row0 : k0;
       const auto krn = k_rsrc(nfirst, nlen);
       const auto vrn = v_rsrc(nfirst, nlen);
-      char* stn = lds + ((kt + 1) & 1) * C::STAGE_BYTES;
+      char* stn = lds + (1 - ST) * C::STAGE_BYTES;
       const uint32_t ntile = (uint32_t)(KR ? nx.lt : kt + 1) * C::BN;
       const uint32_t soffkn = ntile * kstride, soffvn = ntile * vstride;
       // j < NDMA_K: K instruction j of this wave, then the V instructions
@@ -398,6 +406,18 @@ void fwd_mfma_kernel(FwdArgs a) {
           }
       }
       if constexpr (KR) cur = nx;
+    };
+    if constexpr (C::MIN_BLOCKS > 1) {
+      // unrolled by two: constant stages (about 15 fewer VALU instructions
+      // per tile)
+      for (int kt = kt_begin; kt < kt_end; kt += 2) {
+        tile_step(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < kt_end) tile_step(kt + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      // one workgroup per CU (d = 256): the unrolled form's extra registers
+      // cost more than the address arithmetic it saves
+      for (int kt = kt_begin; kt < kt_end; ++kt) tile_step(kt, (kt - kt_begin) & 1);
     }
 
     // epilogue: normalise, LSE, stage O through LDS, full-row stores
