@@ -35,6 +35,8 @@
 // explicitly, so no value read from outside the used rows can reach a sum.
 #include <math.h>
 
+#include <type_traits>
+
 #include "gvattn_internal.h"
 #include "gvattn_mfma.h"
 
@@ -207,8 +209,9 @@ __global__ __launch_bounds__(64 * GF * RB, 2) void bwd_dq_kernel(BwdArgs a) {
     const auto vr = make_rsrc(static_cast<const T*>(a.v) + ((int64_t)k0 * a.g.hkv + kvh) * DV,
                               uk > 0 ? (uint32_t)(uk - 1) * vstride + DV * 2 : 0u);
 
-    auto issue_tile = [&](int kt) {
-      char* st = lds + (kt & 1) * STAGE;
+    // tile kt goes to stage `stage` (the parity of kt, a constant below)
+    auto issue_tile = [&](int kt, int stage) {
+      char* st = lds + stage * STAGE;
       const uint32_t ok = (uint32_t)kt * 32 * kstride, ov = (uint32_t)kt * 32 * vstride;
 #pragma unroll
       for (int i = 0; i < NDMA_K; ++i) {
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(64 * GF * RB, 2) void bwd_dq_kernel(BwdArgs a) {
         if (inst < DMA_V) dma16(vr, st + K_TILE + inst * 1024, voff[i] + ov, 0);
       }
     };
-    if (n_kt > 0) issue_tile(0);
+    if (n_kt > 0) issue_tile(0, 0);
 
     // this lane's query row: Q and dO fragments, D = rowsum(dO * O)
     const int row = wr0 + r32;
@@ -261,11 +264,15 @@ __global__ __launch_bounds__(64 * GF * RB, 2) void bwd_dq_kernel(BwdArgs a) {
     const int lim = a.g.causal ? min(uk, row + uk - uq + 1) : uk;
     const int lim_w = a.g.causal ? min(uk, wr0 + uk - uq + 1) : uk;
 
-    for (int kt = 0; kt < n_kt; ++kt) {
+    // One key tile in stage ST (the next one is loaded into 1 - ST).  The
+    // loop is unrolled by two so that ST is a constant and the LDS operand
+    // addresses are per-lane registers plus immediate offsets.
+    auto tile_step = [&](int kt, auto stage_c) __attribute__((always_inline)) {
+      const int ST = stage_c;
       wait_vmem();
       __syncthreads();
-      if (kt + 1 < n_kt) issue_tile(kt + 1);
-      const char* Ks = lds + (kt & 1) * STAGE;
+      if (kt + 1 < n_kt) issue_tile(kt + 1, 1 - ST);
+      const char* Ks = lds + ST * STAGE;
       const char* Vs = Ks + K_TILE;
 
       // S^T = K Q^T and dP^T = V dO^T: lane (r32, hh) holds query row r32
@@ -299,6 +306,10 @@ __global__ __launch_bounds__(64 * GF * RB, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2)
           dq[db] = E::mfma(read_a_transposed<D, v8>(Ks, a2, db * 32, trow, tcol), dsb[a2], dq[db]);
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+      tile_step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < n_kt) tile_step(kt + 1, std::integral_constant<int, 1>{});
     }
 
     // epilogue: scale, stage through LDS, full-row stores of the used rows
