@@ -337,46 +337,129 @@ void fwd_mfma_kernel(FwdArgs a) {
       const int kbase = KR ? cur.pos + cur.lt * C::BN : kt * C::BN;
       const int lim_t = KR ? min(lim, cur.pos + cur.len) : lim;
       const int lim_wt = KR ? min(lim_w, cur.pos + cur.len) : lim_w;
-      if (kbase + C::BN > lim_wt) {
-        // score (kb, v) is key kbase + kb*32 + 8*(v/4) + 4*hh + v%4: it is
-        // masked when its compile-time offset reaches lim_t - kbase - 4*hh
-        int nv = lim_t - kbase - 4 * hh;
-        asm volatile("" : "+v"(nv));  // defined here: the compares stay in the branch
+      if constexpr (C::MIN_BLOCKS == 1) {
+        // one workgroup per CU (d = 256): mask, then the exact step below
+        // only (a second softmax path cost these variants more registers
+        // than it saved)
+        if (kbase + C::BN > lim_wt) {
+          int nv = lim_t - kbase - 4 * hh;
+          asm volatile("" : "+v"(nv));
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (kb * 32 + 8 * (v >> 2) + (v & 3) >= nv) s[kb][v] = -INFINITY;
+        }
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < C::NKB_; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (kb * 32 + 8 * (v >> 2) + (v & 3) >= nv) s[kb][v] = -INFINITY;
-      }
-
-      // online softmax (exp2 domain), running max raised lazily
-      float mx = -INFINITY;
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+        mx = fmaxf(mx, max_across_halves(mx));
+        const float cand = mx * c;
+        if (__any(cand > m_run + 8.f)) {
+          keep_branch();
+          const float m_new = fmaxf(m_run, cand);
+          const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < C::NKB_; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-      mx = fmaxf(mx, max_across_halves(mx));
-      const float cand = mx * c;
-      if (__any(cand > m_run + 8.f)) {
-        keep_branch();
-        const float m_new = fmaxf(m_run, cand);
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB_; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = exp2_fast(__builtin_fmaf(s[kb][v], c, -m_use));
-          s[kb][v] = p;
-          rs += p;
+          for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
         }
-      l_run += rs;
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float p = exp2_fast(__builtin_fmaf(s[kb][v], c, -m_use));
+            s[kb][v] = p;
+            rs += p;
+          }
+        l_run += rs;
+      } else {
+        auto mask_scores = [&]() __attribute__((always_inline)) {
+          if (kbase + C::BN > lim_wt) {
+            // score (kb, v) is key kbase + kb*32 + 8*(v/4) + 4*hh + v%4: it is
+            // masked when its compile-time offset reaches lim_t - kbase - 4*hh
+            int nv = lim_t - kbase - 4 * hh;
+            asm volatile("" : "+v"(nv));  // defined here: the compares stay in the branch
+#pragma unroll
+            for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+              for (int v = 0; v < 16; ++v)
+                if (kb * 32 + 8 * (v >> 2) + (v & 3) >= nv) s[kb][v] = -INFINITY;
+          }
+        };
+        mask_scores();
+
+        // Online softmax in the exp2 domain.  P = exp2(S*c - m) with m the
+        // running max as it stands: P then exceeds 1 only by the factor the
+        // row's max has grown since m was set, which bf16 P and the FP32 sums
+        // hold easily.  The exact step (tile row max; m raised and O rescaled
+        // when it grew by more than 2^8) runs when a row with keys in this
+        // tile has no m yet, or when some lane's partial row sum leaves
+        // [0, 2^32] (its scores are then recomputed from the K tile).
+        float rs = 0.f;
+        bool exact = __any(m_run == -INFINITY && kbase < lim_t);
+        if (!exact) {
+          // rows without m have no key in this tile: their scores are -inf
+          const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float p = exp2_fast(__builtin_fmaf(s[kb][v], c, -m_use));
+              s[kb][v] = p;
+              rs += p;
+            }
+          exact = __any(!(rs <= 0x1p32f));
+          if (exact) {
+            keep_branch();
+#pragma unroll
+            for (int kb = 0; kb < C::NKB_; ++kb) {
+              s[kb] = f32x16{};
+              const int krow = kb * 32 + r32;
+              const char* kp = Ks + krow * (DQ * 2);
+              const int sw = swz_k<DQ>(krow);
+#pragma unroll
+              for (int kk = 0; kk < C::KK; ++kk)
+                s[kb] = E::mfma(*reinterpret_cast<const v8*>(kp + (((2 * kk + hh) ^ sw) << 4)), qf[kk], s[kb]);
+            }
+            mask_scores();
+          }
+        }
+        if (exact) {
+          keep_branch();
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+          mx = fmaxf(mx, max_across_halves(mx));
+          const float cand = mx * c;
+          if (__any(cand > m_run + 8.f)) {
+            keep_branch();
+            const float m_new = fmaxf(m_run, cand);
+            const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
+          }
+          const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+          rs = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float p = exp2_fast(__builtin_fmaf(s[kb][v], c, -m_use));
+              s[kb][v] = p;
+              rs += p;
+            }
+        }
+        l_run += rs;
+      }
 
       // P^T as 16-bit MFMA operands straight from the score registers
       v8 pb[C::NKB_][2];
