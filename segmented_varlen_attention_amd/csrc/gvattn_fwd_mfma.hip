@@ -394,12 +394,12 @@ void fwd_mfma_kernel(FwdArgs a) {
         mask_scores();
 
         // Online softmax in the exp2 domain.  P = exp2(S*c - m) with m the
-        // running max as it stands: P then exceeds 1 only by the factor the
-        // row's max has grown since m was set, which bf16 P and the FP32 sums
-        // hold easily.  The exact step (tile row max; m raised and O rescaled
-        // when it grew by more than 2^8) runs when a row with keys in this
-        // tile has no m yet, or when some lane's partial row sum leaves
-        // [0, 2^32] (its scores are then recomputed from the K tile).
+        // running max as it stands: P then exceeds 1 by the factor the row's
+        // max has grown since m was set.  The exact step (tile row max; m
+        // raised and O rescaled when it grew by more than 2^8) runs when a
+        // row with keys in this tile has no m yet, or when some lane's
+        // partial row sum leaves [0, 2^15] (its scores are then recomputed
+        // from the K tile), so that every weight stays within fp16 range.
         float rs = 0.f;
         bool exact = __any(m_run == -INFINITY && kbase < lim_t);
         if (!exact) {
@@ -413,7 +413,7 @@ void fwd_mfma_kernel(FwdArgs a) {
               s[kb][v] = p;
               rs += p;
             }
-          exact = __any(!(rs <= 0x1p32f));
+          exact = __any(!(rs <= 0x1p15f));  // every weight <= 2^15: fp16 holds it
           if (exact) {
             keep_branch();
 #pragma unroll

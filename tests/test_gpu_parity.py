@@ -110,6 +110,32 @@ def test_many_segments_tiny_lengths(nseg):
                                             derived=True))
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_jumps_across_key_tiles(dtype, d, causal):
+    """Key tiles whose scores are 32x larger (or smaller) than the previous
+    tile's: the running max a tile's softmax starts from is then about 2^20
+    below the tile's largest weight, the row sums overflow the bound the
+    kernel accepts (2^15, which keeps fp16 weights finite) and the tile is
+    redone by the exact step (scores recomputed, max raised, O rescaled);
+    tiles far below the max underflow to zero weight."""
+    seed = 1200 + d + 7 * causal + (3 if dtype == W.FP16 else 0)
+    uq, uk = [96, 70, 40, 33], [260, 200, 97, 65]
+    wl = W.random_small(seed, 4, 96, 260, 8, 2, d, causal, dtype, lengths=(uq, uk))
+    g = wl.geom
+    factors = np.array([0.25, 8.0, 0.25, 1.0, 8.0, 0.5, 0.25, 8.0, 2.0])
+    k = wl.k.copy()
+    for seg in range(g.nseg):
+        k0 = int(g.cu_k[seg])
+        j = np.arange(int(g.cu_k[seg + 1]) - k0)
+        k[k0 + j] *= factors[(j // 32) % len(factors)][:, None, None]
+    wl.k = W.round_to(dtype, k)
+    out, lse, _ = DeviceCase(wl).fwd()
+    say(f"[score jumps {dtype} d{d} c{int(causal)}]",
+        compare_full(out, lse, wl, where=f"score jumps {dtype} d{d} c{int(causal)}", derived=True))
+
+
 # --- the five workloads -------------------------------------------------------------
 
 def test_config1_fp32():
