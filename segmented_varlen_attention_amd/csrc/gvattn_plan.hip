@@ -31,6 +31,7 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 // Forward entries are ordered by cost in groups of 2^kGroupShift key tiles,
 // then by segment.
 constexpr int kGroupShift = 3;
+constexpr int kExactCost = 16;  // a multiple of 2^kGroupShift
 // Segments whose lengths, splits and entry offsets the plan keeps in LDS;
 // a launch with more segments reads them from global memory instead.
 constexpr int kPlanLdsSegs = 2048;
@@ -282,11 +283,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // segments' K/V in its L2 while the order stays longest first to within
   // the coarsening.  Otherwise (and for the key-tile plan) the key is the
   // cost.
-  const bool grouped = a.mode == 0 &&
-                       ((long long)(min(s_max_kt, kCostBuckets - 1) >> kGroupShift) + 1) * nseg <=
-                           kCostBuckets;
+  // Entries below kExactCost key tiles (the last rounds of the schedule)
+  // keep their exact cost order, which keeps the end of the launch even.
+  const int max_kt = min(s_max_kt, kCostBuckets - 1);
+  const bool grouped =
+      a.mode == 0 && max_kt >= kExactCost &&
+      kExactCost + ((long long)(max_kt >> kGroupShift) - (kExactCost >> kGroupShift) + 1) * nseg <=
+          kCostBuckets;
   auto sort_key = [&](int cost, int s) {
-    return grouped ? (cost >> kGroupShift) * nseg + (nseg - 1 - s) : cost;
+    if (!grouped || cost < kExactCost) return cost;
+    return kExactCost + ((cost >> kGroupShift) - (kExactCost >> kGroupShift)) * nseg + (nseg - 1 - s);
   };
   for (int t = tid; t < n_tiles; t += kPlanThreads) {
     const int s = find_segment(v.off, nseg, t);
