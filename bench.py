@@ -7,12 +7,15 @@ used q/k lengths uniform in [0, 2048] (4 segments without keys), 32 q heads /
 over used rows: every visible (query, key) pair costs 4*d FLOPs per query
 head; masked, gap and padding work is never counted.
 
-Prints one JSON line.  ``--config N`` benches another workload (2, 4, 5:
-4 times the two partition launches plus the LSE merge, or with ``--fused``
-one key-range launch over both partitions; 6: the Ulysses rank-major joint
-attention of issue #18687 through the key-range entry point; 7: a
-decode-like batch that the plan splits along the keys, reported against
-the HBM roofline);
+Prints one JSON line.  ``--workload NAME`` benches another workload:
+cfg_cross_attention (2 CFG samples of 4096 queries over right-padded text
+of 24 and 700 keys), multiview_partitions (8 x 8190 queries over two key
+partitions of 16380, the two partition launches plus the LSE merge, or with
+``--fused`` one key-range launch over both), large_head_d256 (16 segments
+of 16384, d = 256), ulysses_joint (the Ulysses rank-major joint attention of
+issue #18687 through the key-range entry point) and decode_batch (32
+segments of 4 query rows over 4096-16384 keys, which the plan splits along
+the keys; reported against the HBM roofline).
 ``--dtype fp16`` runs the same workload through the fp16 matrix-core path
 (the bf16-exact draws converted to fp16).
 """
@@ -112,9 +115,11 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=0.2,
                     help="default warmup length: after the inputs are written the shader "
                          "clock takes about 50 ms of load to settle")
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", default="causal_replay",
+                    choices=["causal_replay", "cfg_cross_attention", "multiview_partitions",
+                             "large_head_d256", "ulysses_joint", "decode_batch"])
     ap.add_argument("--fused", action="store_true",
-                    help="config 4: both partitions as key ranges of one launch")
+                    help="multiview_partitions: both partitions as key ranges of one launch")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true",
@@ -126,7 +131,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: there is no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -153,10 +158,11 @@ def main():
         return
 
     t0 = time.time()
-    wl = (W.ulysses_joint() if args.config == 6 else
-          W.decode_batch() if args.config == 7 else W.CONFIGS[args.config]())
+    wk = args.workload
+    wl = (W.ulysses_joint() if wk == "ulysses_joint" else
+          W.decode_batch() if wk == "decode_batch" else W.WORKLOADS[wk]())
     g = wl.geom
-    fused = args.config == 4 and args.fused
+    fused = wk == "multiview_partitions" and args.fused
     if fused:
         (cu_a, used_a), (cu_b, used_b) = wl.partitions
         wl.key_ranges = (np.arange(0, 2 * g.nseg + 1, 2, dtype=np.int32),
@@ -197,7 +203,7 @@ def main():
         launches = []
         parts = [(out, lse)]
         wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode, d_v=g.dv)]
-    elif args.config == 4:
+    elif wk == "multiview_partitions":
         launches = [(up(cu), up(u)) for cu, u in wl.partitions]
         parts = [(torch.empty_like(out), torch.empty_like(lse)) for _ in launches]
         wss = [gv.alloc_workspace(g.nseg, g.total_q, g.hq, g.hkv, g.d, dcode, d_v=g.dv)
@@ -215,7 +221,7 @@ def main():
         for (cu_k, used_k), (o, l), ws in zip(launches, parts, wss):
             gv.gvattn_fwd(q, k, v, cu_q, cu_k, used_q, used_k, o, l, float(g.scale), g.causal,
                           workspace=ws)
-        if args.config == 4:
+        if wk == "multiview_partitions":
             gv.gvattn_lse_merge([p[0] for p in parts], [p[1] for p in parts], cu_q, used_q, out,
                                 lse)
 
@@ -227,7 +233,7 @@ def main():
         gv.gvattn_fwd_run(q, k, v, cu_q, cu_k, used_q, used_k, o, l, float(g.scale), g.causal,
                           ws)
 
-    if args.config == 4 and not fused:
+    if wk == "multiview_partitions" and not fused:
         flops = sum(flops_of(g.used_q, u) for _, u in wl.partitions)
 
     # Warmup.  Right after the input upload and the sentinel fills (or any
@@ -267,11 +273,11 @@ def main():
     torch.cuda.synchronize()
     kern_ms = k0.elapsed_time(k1) / args.steps
     kern_flops = (flops_of(g.used_q, launches[0][1].cpu().numpy())
-                  if (args.config == 4 and not fused) else flops)
+                  if (wk == "multiview_partitions" and not fused) else flops)
     log(f"[bench] main kernel alone: {kern_ms:.4f} ms/launch")
 
     merge_rec = None
-    if args.config == 4 and not fused:
+    if wk == "multiview_partitions" and not fused:
         # the LSE merge alone: algorithmic bytes = both partials, the output
         # and the LSEs, used rows only
         m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -290,7 +296,7 @@ def main():
         log(f"[bench] LSE merge alone: {merge_ms:.4f} ms, {merge_rec['GB_per_s']} GB/s")
 
     bwd_rec = None
-    if (not args.no_bwd and wl.key_ranges is None and args.config != 4 and g.d <= 128
+    if (not args.no_bwd and wl.key_ranges is None and wk != "multiview_partitions" and g.d <= 128
             and g.dv <= 128):
         # gradients of the same step: dO seeded, O / LSE from the forward
         # above; FLOPs counted as the five products of the calculus (S, dP,
@@ -321,26 +327,26 @@ def main():
 
     tflops = flops / (ms * 1e-3) / 1e12
     achieved = kern_flops / (kern_ms * 1e-3) / 1e12
-    traffic_rec = recorded_traffic() if (args.config == 3 and args.dtype == "bf16") else None
+    traffic_rec = recorded_traffic() if (wk == "causal_replay" and args.dtype == "bf16") else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": (traffic_rec["bytes_per_launch"] if traffic_rec else None)}
-    if args.config == 7:  # memory-bound: algorithmic bytes over the whole call
+    if wk == "decode_batch":  # memory-bound: algorithmic bytes over the whole call
         gbs = algorithmic_bytes(g) / (kern_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
-    names = {2: "bf16_cfg_cross_attn_b2_4096q_text24_700_gqa32x8_d128",
-             3: "bf16_causal_gapped_replay_64x2048_gqa32x8_d128",
-             4: "bf16_multiview_8x8190q_32760k_2partitions_merge_gqa24x8_d128",
-             5: "bf16_gapped_16x16384_gqa16x4_d256",
-             6: "bf16_ulysses2_rank_major_joint_b2_4096q_text4096_video4096_keyranges",
-             7: "bf16_decode_b32x4_k4096_16384_gqa32x8_d128_causal_splitk"}
+    names = {"cfg_cross_attention": "bf16_cfg_cross_attn_b2_4096q_text24_700_gqa32x8_d128",
+             "causal_replay": "bf16_causal_gapped_replay_64x2048_gqa32x8_d128",
+             "multiview_partitions": "bf16_multiview_8x8190q_32760k_2partitions_merge_gqa24x8_d128",
+             "large_head_d256": "bf16_gapped_16x16384_gqa16x4_d256",
+             "ulysses_joint": "bf16_ulysses2_rank_major_joint_b2_4096q_text4096_video4096_keyranges",
+             "decode_batch": "bf16_decode_b32x4_k4096_16384_gqa32x8_d128_causal_splitk"}
     res = {
         "metric": "gapped varlen attn fwd TFLOP/s (used rows) + % of MI355X bf16 MFMA peak",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
-        "config": {"workload": names[args.config].replace("bf16", args.dtype, 1)
+        "config": {"workload": names[wk].replace("bf16", args.dtype, 1)
                    + ("_fused_keyranges" if fused else ""),
                    "segments": g.nseg,
                    "used_q_rows": int(np.sum(g.used_q)), "hq": g.hq, "hkv": g.hkv, "d": g.d,
@@ -354,7 +360,7 @@ def main():
         res["merge"] = merge_rec
     if bwd_rec is not None:
         res["backward"] = bwd_rec
-    if not args.no_cpu_baseline and args.config == 3 and args.dtype == "bf16":
+    if not args.no_cpu_baseline and wk == "causal_replay" and args.dtype == "bf16":
         log("[bench] timing the oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_seconds)
     print(json.dumps(res), flush=True)

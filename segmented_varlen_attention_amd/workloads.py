@@ -194,7 +194,7 @@ def fill_qkv(geom: Geometry, seed: int, std: float = 1.0, threads=None):
 
 # --- the five workloads -----------------------------------------------------
 
-def config1() -> Workload:
+def fp32_three_segments() -> Workload:
     """FP32, 3 segments of capacity 64; used q {40,64,13}, used k {50,0,64};
     8 q heads / 2 KV heads, d=64; the middle segment has no keys."""
     seed = 1  # lengths are fixed; only Q/K/V are drawn
@@ -205,7 +205,7 @@ def config1() -> Workload:
                     note="segment index 1 has zero keys")
 
 
-def config2() -> Workload:
+def cfg_cross_attention() -> Workload:
     """BF16 CFG cross-attention, batch 2: 4096 video queries per sample attend
     right-padded text K/V of capacity 4096 with real lengths 24 and 700; pad
     K/V slots are exactly zero; 32 q heads / 8 KV heads, d=128."""
@@ -222,7 +222,7 @@ def config2() -> Workload:
                     note="pad-slot K/V exactly zero (text LLM zeroes pad rows)")
 
 
-def config3_lengths(seed: int = 3, nseg: int = 64, cap: int = 2048):
+def causal_replay_lengths(seed: int = 3, nseg: int = 64, cap: int = 2048):
     rng = np.random.default_rng(seed)
     uq = rng.integers(0, cap, size=nseg, endpoint=True).astype(np.int32)
     uk = rng.integers(0, cap, size=nseg, endpoint=True).astype(np.int32)
@@ -231,18 +231,18 @@ def config3_lengths(seed: int = 3, nseg: int = 64, cap: int = 2048):
     return uq, uk
 
 
-def config3() -> Workload:
+def causal_replay() -> Workload:
     """BF16 causal gapped replay: 64 segments of capacity 2048, used q and k
     lengths uniform in [0, 2048] with 4 segments forced to zero keys; causal
     mask aligned bottom-right in each segment; 32 q heads / 8 KV heads, d=128."""
     seed = 3
-    uq, uk = config3_lengths(seed)
+    uq, uk = causal_replay_lengths(seed)
     g = make_geometry([2048] * 64, [2048] * 64, uq, uk, 32, 8, 128, causal=True)
     q, k, v = fill_qkv(g, seed)
     return Workload("bf16_causal_replay_64x2048", seed, g, q, k, v)
 
 
-def config4() -> Workload:
+def multiview_partitions() -> Workload:
     """BF16 multiview joint attention: 8 segments (7 camera views + 1 LiDAR
     stream) with 8190 used query rows and 32760 keys each, keys split into
     visibility partition A (first 16380) and B (the rest); 24 q heads / 8 KV
@@ -260,25 +260,27 @@ def config4() -> Workload:
                     partitions=[(cu_a, used), (cu_b, used.copy())])
 
 
-def config5_lengths(seed: int = 5, nseg: int = 16, cap: int = 16384):
+def large_head_lengths(seed: int = 5, nseg: int = 16, cap: int = 16384):
     rng = np.random.default_rng(seed)
     uq = rng.integers(cap // 2, cap, size=nseg, endpoint=True).astype(np.int32)
     uk = rng.integers(0, cap, size=nseg, endpoint=True).astype(np.int32)
     return uq, uk
 
 
-def config5() -> Workload:
+def large_head_d256() -> Workload:
     """BF16 large-head gapped varlen attention, non-causal: 16 segments of
     capacity 16384, used q uniform in [8192, 16384], used k uniform in
     [0, 16384]; 16 q heads / 4 KV heads, d=256; values N(0, 0.5^2)."""
     seed = 5
-    uq, uk = config5_lengths(seed)
+    uq, uk = large_head_lengths(seed)
     g = make_geometry([16384] * 16, [16384] * 16, uq, uk, 16, 4, 256, causal=False)
     q, k, v = fill_qkv(g, seed, std=0.5)
     return Workload("bf16_d256_gapped_16x16384", seed, g, q, k, v)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {"fp32_three_segments": fp32_three_segments, "cfg_cross_attention": cfg_cross_attention,
+             "causal_replay": causal_replay, "multiview_partitions": multiview_partitions,
+             "large_head_d256": large_head_d256}
 
 
 def ulysses_joint(seed: int = 6, ranks: int = 2, text_cap: int = 4096, video: int = 4096,

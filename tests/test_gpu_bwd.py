@@ -196,14 +196,14 @@ def test_bwd_causal_replay_full_size_sampled():
     the oracle's; the rest come from the GPU forward (they only feed their
     own segments' gradients)."""
     t = torch()
-    wl = W.config3()
+    wl = W.causal_replay()
     g = wl.geom
     used = np.nonzero((g.used_q > 0) & (g.used_k > 0))[0]
     s_long = int(used[np.argmax(g.used_q[used] + g.used_k[used])])
     s_short = int(used[np.argmin(g.used_q[used])])
     below = used[g.used_k[used] < g.used_q[used]]
     picks = sorted({s_long, s_short} | ({int(below[0])} if len(below) else set()))
-    say(f"[bwd config3] segments {picks}: used_q {g.used_q[picks].tolist()} "
+    say(f"[bwd causal_replay] segments {picks}: used_q {g.used_q[picks].tolist()} "
         f"used_k {g.used_k[picks].tolist()}")
     q_, k_, v_ = upload(wl.q, g), upload(wl.k, g), upload(wl.v, g)
     out = t.zeros((g.total_q, g.hq, g.dv), dtype=t.bfloat16, device="cuda")
@@ -239,8 +239,8 @@ def test_bwd_causal_replay_full_size_sampled():
         for name, got, want, mag in (("dq", dq[q0:q0 + uq], rq, aq), ("dk", dk[k0:k0 + uk], rk, ak),
                                      ("dv", dv[k0:k0 + uk], rv, av)):
             m = np.ones(want.shape[0], dtype=bool)
-            st[name] = check_grad(to_np(got), want, mag, m, W.BF16, f"config3 seg {s} {name}")
-        say(f"[bwd config3] seg {s}", st)
+            st[name] = check_grad(to_np(got), want, mag, m, W.BF16, f"causal_replay seg {s} {name}")
+        say(f"[bwd causal_replay] seg {s}", st)
 
 
 def test_bwd_cross_attention_split():
@@ -249,5 +249,5 @@ def test_bwd_cross_attention_split():
     tiles, so the dK / dV loop of every tile is split into chunks whose FP32
     partials a reduce pass sums.  Every used row and key against the
     oracle; pad keys keep their sentinel."""
-    wl = W.config2()
+    wl = W.cfg_cross_attention()
     check_case(wl, 990, "bwd cross-attention split")

@@ -138,26 +138,26 @@ def test_score_jumps_across_key_tiles(dtype, d, causal):
 
 # --- the five workloads -------------------------------------------------------------
 
-def test_config1_fp32():
-    wl = W.config1()
+def test_fp32_three_segments():
+    wl = W.fp32_three_segments()
     out, lse, _ = DeviceCase(wl).fwd()
-    st = compare_full(out, lse, wl, where="config1")
-    say("[config1]", st)
+    st = compare_full(out, lse, wl, where="fp32_three_segments")
+    say("[fp32_three_segments]", st)
     lse_np = to_np(lse)
     g = wl.geom
     rows = slice(g.cu_q[1], g.cu_q[1] + g.used_q[1])  # the segment with no keys
     assert np.all(np.isneginf(lse_np[:, rows])) and np.all(to_np(out)[rows] == 0.0)
 
 
-def test_config2_cfg_cross_attention():
-    wl = W.config2()
+def test_cfg_cross_attention():
+    wl = W.cfg_cross_attention()
     g = wl.geom
     dc = DeviceCase(wl)
     out, lse, _ = dc.fwd()
     o_ref, l_ref = oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k,
                                         float(g.scale), False, workers=16)
-    st = compare_full(out, lse, wl, o_ref=o_ref, l_ref=l_ref, where="config2")
-    say("[config2]", st)
+    st = compare_full(out, lse, wl, o_ref=o_ref, l_ref=l_ref, where="cfg_cross_attention")
+    say("[cfg_cross_attention]", st)
     # equals attention over the text trimmed per sample, not the unmasked form
     lens = [int(x) for x in g.used_k]
     keep = np.concatenate([np.arange(g.cu_k[s], g.cu_k[s] + L) for s, L in enumerate(lens)])
@@ -165,7 +165,7 @@ def test_config2_cfg_cross_attention():
     o_t, l_t = oracle.attention_fwd(wl.q, wl.k[keep], wl.v[keep], g.cu_q, cu_t, g.used_q, lens,
                                     float(g.scale), False, workers=16)
     o_gpu, l_gpu = to_np(out), to_np(lse)
-    compare(o_gpu, l_gpu, o_t, l_t, W.BF16, "config2 vs trimmed")
+    compare(o_gpu, l_gpu, o_t, l_t, W.BF16, "cfg_cross_attention vs trimmed")
     # the unmasked (buggy) result differs measurably for the short sample
     gb = g.with_keys(g.cu_k, [4096, 4096])
     ob, lb = oracle.attention_fwd(wl.q[:4096], wl.k[:4096], wl.v[:4096], g.cu_q[:2],
@@ -174,8 +174,8 @@ def test_config2_cfg_cross_attention():
     assert np.max(np.abs(l_gpu[:, :4096] - lb)) > 1.0
 
 
-def test_config3_causal_replay():
-    wl = W.config3()
+def test_causal_replay_64x2048():
+    wl = W.causal_replay()
     g = wl.geom
     out, lse, ws = DeviceCase(wl).fwd()
     assert B.gvattn_read_device_error(ws) == 0
@@ -183,8 +183,8 @@ def test_config3_causal_replay():
     big = [int(s) for s in np.argsort(-(g.used_q.astype(np.int64) * g.used_k))[:3]]
     more = [s for s in (5, 17, 33, 48, 63) if s not in big + empty]
     samples = [(s, np.arange(g.used_q[s])) for s in empty + big + more]
-    st = compare_sampled(out, lse, wl, samples, where="config3")
-    say("[config3]", st)
+    st = compare_sampled(out, lse, wl, samples, where="causal_replay")
+    say("[causal_replay]", st)
     # any size: all used rows finite; rows with no visible key exactly (0, -inf)
     m = used_row_mask(g)
     t = torch()
@@ -200,8 +200,8 @@ def test_config3_causal_replay():
             assert (out[r0:r0 + n_dead] == 0).all().item(), s
 
 
-def test_config4_partitions_merge():
-    wl = W.config4()
+def test_multiview_partitions_merge():
+    wl = W.multiview_partitions()
     g = wl.geom
     dc = DeviceCase(wl)
     (cu_a, used_a), (cu_b, used_b) = wl.partitions
@@ -218,22 +218,22 @@ def test_config4_partitions_merge():
     rng = np.random.default_rng(44)
     samples = [(s, np.sort(rng.choice(8190, 12, replace=False))) for s in range(8)]
     samples[0] = (0, np.array([0, 1, 8188, 8189]))
-    st_m = compare_sampled(out_m, lse_m, wl, samples, where="config4 merged")
-    st_s = compare_sampled(out_s, lse_s, wl, samples, where="config4 single")
-    say("[config4] merged", st_m, "single", st_s)
+    st_m = compare_sampled(out_m, lse_m, wl, samples, where="multiview_partitions merged")
+    st_s = compare_sampled(out_s, lse_s, wl, samples, where="multiview_partitions single")
+    say("[multiview_partitions] merged", st_m, "single", st_s)
     # partitions against their own oracle
-    st_a = compare_sampled(out_a, lse_a, wl, samples[:3], geom=ga, where="config4 A")
-    say("[config4] A", st_a)
+    st_a = compare_sampled(out_a, lse_a, wl, samples[:3], geom=ga, where="multiview_partitions A")
+    say("[multiview_partitions] A", st_a)
     # merged vs single pass on the device, all rows
     t = torch()
     d_lse = (lse_m - lse_s).abs().max().item()
     d_out = (out_m.float() - out_s.float()).abs().max().item()
-    say(f"[config4] merged-vs-single max |dLSE|={d_lse:.3g} max |dO|={d_out:.3g}")
+    say(f"[multiview_partitions] merged-vs-single max |dLSE|={d_lse:.3g} max |dO|={d_out:.3g}")
     assert d_lse <= 2e-5 and d_out <= 1.6e-2
 
 
-def test_config5_large_head():
-    wl = W.config5()
+def test_large_head_d256():
+    wl = W.large_head_d256()
     g = wl.geom
     out, lse, ws = DeviceCase(wl).fwd()
     assert B.gvattn_read_device_error(ws) == 0
@@ -243,8 +243,8 @@ def test_config5_large_head():
         uq = int(g.used_q[s])
         rows = np.unique(np.concatenate([[0, uq - 1], rng.choice(uq, 6, replace=False)]))
         samples.append((s, rows))
-    st = compare_sampled(out, lse, wl, samples, where="config5")
-    say("[config5]", st)
+    st = compare_sampled(out, lse, wl, samples, where="large_head_d256")
+    say("[large_head_d256]", st)
 
 
 # --- robustness ---------------------------------------------------------------------

@@ -138,7 +138,7 @@ def test_ulysses_rank_major_joint():
 def test_fused_partitions_single_launch():
     """The multiview workload's two visibility partitions as two key ranges
     per segment: one launch, no merge.  Sampled rows against the oracle."""
-    wl = W.config4()
+    wl = W.multiview_partitions()
     g = wl.geom
     (cu_a, used_a), (cu_b, used_b) = wl.partitions
     starts = np.stack([cu_a[:-1], cu_b[:-1]], axis=1).reshape(-1).astype(np.int32)

@@ -281,7 +281,7 @@ def test_unmasked_zero_pads_closed_form(golden):
 def test_empty_segment_and_gap_rows(golden):
     """Gap rows keep the sentinel bit for bit; a segment with no keys gets
     O = 0 and LSE = -inf (PR #302)."""
-    wl = W.config1()
+    wl = W.fp32_three_segments()
     g = wl.geom
     o, l = run_oracle(wl)
     sent = golden["gap_rows_untouched"]["sentinel"]
@@ -407,8 +407,8 @@ def test_merge_closed_form_two_parts():
     assert np.all(om == 0.0) and lm[0, 0] == -np.inf
 
 
-def test_flop_count_config1():
-    g = W.config1().geom
+def test_flop_count_fp32_three_segments():
+    g = W.fp32_three_segments().geom
     assert oracle.attention_flops(g.used_q, g.used_k, g.hq, g.d, g.dv, False) == 5_799_936
     # causal counts only visible pairs: uq=3, uk=5 -> rows see 3, 4, 5 keys
     assert oracle.attention_flops([3], [5], 1, 1, 1, True) == 12 * 4
