@@ -142,15 +142,17 @@ int gvattn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
 
 /*
  * The two halves of gvattn_fwd, for callers that replay one geometry many
- * times (PR #302, "What": the gather is built once per launch and fold, so
- * segment lengths are read once per plan rather than at every step).
+ * times: the segment lengths are then read once, by the plan, instead of at
+ * every launch (the PR #302 review asks for segment geometry that is not
+ * read back to the host on every call).
  *
  * gvattn_fwd_plan reads only the geometry arrays and writes the sorted tile
  * work list into the workspace.  gvattn_fwd_run takes the same arguments as
  * gvattn_fwd and runs the attention on the plan found in the workspace; the
  * geometry arrays must hold the values the plan was built from.  A plan
- * built for a different tile shape, head count, causal flag or segment count
- * is detected on the device: the run writes nothing and sets
+ * built for any other host-side geometry (element type's tile shape, hq,
+ * hkv, d, d_v, causal flag, segment count, total_q, total_k or workspace
+ * layout) is detected on the device: the run writes nothing and sets
  * GVATTN_DEVERR_PLAN.
  */
 int gvattn_fwd_plan(int32_t dtype,
@@ -170,10 +172,10 @@ int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * Forward over key ranges (TensorRT-LLM issue #18687, "Suggested fix", item
- * 1: after the Ulysses all-to-all the key order is rank-major, so a sample's
- * valid keys are several runs of rows, not one prefix).  Plan + attention
- * in one call, as gvattn_fwd.
+ * Forward over key ranges (TensorRT-LLM issue #18687, "additional notes",
+ * first of the possible fixes: the Ulysses exchange leaves keys ordered by
+ * rank, so a sample's valid keys are several runs of rows rather than one
+ * prefix).  Plan + attention in one call, as gvattn_fwd.
  *
  * Segment s's keys are the concatenation, in list order, of the K/V row
  * ranges [kr_start[i], kr_start[i] + kr_len[i]) for i in [kr_off[s],

@@ -97,6 +97,24 @@ int check_workspace(const void* ws, size_t bytes, const WsLayout& L) {
 // keys per key tile of the forward kernel (split-K chunks are whole tiles)
 int key_tile(int32_t d, int32_t dv) { return (d <= 128 && dv <= 128) ? 32 : 64; }
 
+// The plan key of a geometry: the run side recomputes it and refuses a plan
+// built for anything else (another head layout, row total or workspace
+// layout included).
+uint32_t geometry_key(int rows, const Geometry& g, const WsLayout& L, int flags) {
+  PlanKeyArgs k;
+  k.rows = rows;
+  k.causal = g.causal;
+  k.nseg = g.nseg;
+  k.flags = flags | (g.d << 1) | (g.dv << 10);
+  k.hq = g.hq;
+  k.hkv = g.hkv;
+  k.total_q = g.total_q;
+  k.total_k = g.total_k;
+  k.splits = L.splits;
+  k.max_tiles = L.max_tiles;
+  return plan_key(k);
+}
+
 Geometry make_geom(const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
                    const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
                    int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t causal) {
@@ -132,7 +150,7 @@ int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
   a.max_tiles = (int32_t)L.max_tiles;
   a.key_tile = key_tile(g.d, g.dv);
   a.n_head_chunks = g.hq / t.gf;
-  a.key = plan_key(t.rows, g.causal, g.nseg, (g.kr_off != nullptr) | (g.d << 1) | (g.dv << 10));
+  a.key = geometry_key(t.rows, g, L, g.kr_off != nullptr ? 1 : 0);
   const int dmax = g.d > g.dv ? g.d : g.dv;
   a.q_row_bytes = (int64_t)g.hq * dmax * esize(dtype);
   a.k_row_bytes = (int64_t)g.hkv * dmax * esize(dtype);
@@ -152,7 +170,7 @@ int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   a.out = out;
   a.lse = lse;
   a.scale_log2 = scale * kLog2e;
-  a.key = plan_key(t.rows, g.causal, g.nseg, (g.kr_off != nullptr) | (g.d << 1) | (g.dv << 10));
+  a.key = geometry_key(t.rows, g, L, g.kr_off != nullptr ? 1 : 0);
   a.n_head_chunks = g.hq / t.gf;
   const int64_t max_work = L.max_tiles * L.splits * a.n_head_chunks;
   bool ok = false;
@@ -203,7 +221,6 @@ int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   const BwdLayout L = bwd_layout_of(dtype, g.nseg, g.total_q, g.total_k, g.hq, g.hkv, g.d, g.dv);
   char* base = static_cast<char*>(ws);
   const int dmax = g.d > g.dv ? g.d : g.dv;
-  const int shape_flags = (g.d << 1) | (g.dv << 10);
 
   PlanArgs pq;
   pq.g = g;
@@ -214,7 +231,7 @@ int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   pq.max_tiles = (int32_t)L.q.max_tiles;
   pq.key_tile = 32;
   pq.n_head_chunks = g.hq / t.gf;
-  pq.key = plan_key(t.rows, g.causal, g.nseg, shape_flags | kPlanBwdQ);
+  pq.key = geometry_key(t.rows, g, L.q, kPlanBwdQ);
   pq.q_row_bytes = (int64_t)g.hq * dmax * esize(dtype);
   pq.k_row_bytes = (int64_t)g.hkv * dmax * esize(dtype);
   PlanArgs pk = pq;
@@ -224,7 +241,7 @@ int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   pk.rows = kBwdKeyRows;
   pk.max_tiles = (int32_t)L.k.max_tiles;
   pk.n_head_chunks = g.hkv;
-  pk.key = plan_key(kBwdKeyRows, g.causal, g.nseg, shape_flags | kPlanBwdK);
+  pk.key = geometry_key(kBwdKeyRows, g, L.k, kPlanBwdK);
   if (launch_plan(pq, stream) != hipSuccess) return GVATTN_ERR_HIP;
   if (launch_plan(pk, stream) != hipSuccess) return GVATTN_ERR_HIP;
 

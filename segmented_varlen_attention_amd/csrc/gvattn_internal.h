@@ -75,13 +75,32 @@ inline TileShape choose_shape(int dtype, int hq, int hkv, int d) {
   return t;
 }
 
-inline uint32_t plan_key(int rows, int causal, int nseg, int ranges) {
+// Binds a plan to everything the run side derives from host sizes: tile
+// shape, causal flag, segment count, variant flags (key ranges, head dims,
+// backward plan kind), head counts, row totals and the workspace layout
+// (split capacity and list length).  A run whose key differs from the one
+// the plan stored refuses to read the plan.
+struct PlanKeyArgs {
+  int rows, causal, nseg, flags, hq, hkv, total_q, total_k, splits;
+  int64_t max_tiles;
+};
+
+inline uint32_t plan_key(const PlanKeyArgs& k) {
   uint32_t h = 2166136261u;
-  auto mix = [&h](uint32_t x) { h = (h ^ x) * 16777619u; };
-  mix((uint32_t)rows);
-  mix((uint32_t)causal);
-  mix((uint32_t)nseg);
-  mix((uint32_t)ranges);
+  auto mix = [&h](uint32_t x) {
+    for (int i = 0; i < 4; ++i) h = (h ^ ((x >> (8 * i)) & 0xffu)) * 16777619u;
+  };
+  mix((uint32_t)k.rows);
+  mix((uint32_t)k.causal);
+  mix((uint32_t)k.nseg);
+  mix((uint32_t)k.flags);
+  mix((uint32_t)k.hq);
+  mix((uint32_t)k.hkv);
+  mix((uint32_t)k.total_q);
+  mix((uint32_t)k.total_k);
+  mix((uint32_t)k.splits);
+  mix((uint32_t)k.max_tiles);
+  mix((uint32_t)(k.max_tiles >> 32));
   return h | 1u;  // never 0, so a zeroed workspace never matches
 }
 
