@@ -373,6 +373,97 @@ def test_merge_small(pdt, odt, nparts):
     check_gap_rows(out, lse, g)
 
 
+def test_merge_nan_lse_rows():
+    """A NaN LSE in one partial (PR #312's FP32 LSE merge, with NaN
+    propagation as the convention): exactly those (row, head) pairs come out
+    NaN in O and LSE, whichever partial holds the NaN; every other used pair
+    is bit-identical to the merge of the same partials without the NaN, and
+    gap rows keep the sentinel."""
+    t = torch()
+    wl = W.random_small(410, 4, 40, 70, 8, 2, 128, False, W.BF16,
+                        lengths=([40, 0, 23, 31], [70, 30, 9, 0]))
+    g = wl.geom
+    dc = DeviceCase(wl)
+    half = [u // 2 for u in g.used_k]
+    parts = []
+    for cu, used in ((g.cu_k, half),
+                     (np.array([g.cu_k[s] + half[s] for s in range(g.nseg)] + [g.total_k]),
+                      [int(g.used_k[s]) - half[s] for s in range(g.nseg)])):
+        o, l, _ = dc.fwd(g.with_keys(cu, used))
+        parts.append((o, l))
+    clean_o, clean_l = dc.new_out()
+    B.gvattn_lse_merge([p[0] for p in parts], [p[1] for p in parts], dc.cu_q, dc.used_q,
+                       clean_o, clean_l)
+    # (row, head) pairs: used rows of segments 0 and 2, one head each
+    nan_at = [(int(g.cu_q[0]) + 3, 1), (int(g.cu_q[0]) + 39, 6), (int(g.cu_q[2]) + 5, 0)]
+    for holder in (0, 1):
+        lses = [p[1].clone() for p in parts]
+        for r, h in nan_at:
+            lses[holder][h, r] = float("nan")
+        out, lse = dc.new_out()
+        B.gvattn_lse_merge([p[0] for p in parts], lses, dc.cu_q, dc.used_q, out, lse)
+        t.cuda.synchronize()
+        check_gap_rows(out, lse, g)
+        o_np, l_np = to_np(out), to_np(lse)
+        mask = np.zeros((g.total_q, g.hq), bool)
+        for r, h in nan_at:
+            mask[r, h] = True
+            assert np.isnan(o_np[r, h]).all() and np.isnan(l_np[h, r]), (holder, r, h)
+        used = used_row_mask(g)
+        keep = used[:, None] & ~mask
+        assert not np.isnan(o_np[keep]).any() and not np.isnan(l_np.T[keep]).any()
+        assert np.array_equal(out.view(t.int16).cpu().numpy()[keep],
+                              clean_o.view(t.int16).cpu().numpy()[keep])
+        assert np.array_equal(lse.view(t.int32).cpu().numpy().T[keep],
+                              clean_l.view(t.int32).cpu().numpy().T[keep])
+    say("[merge NaN LSE] NaN rows", nan_at, "isolated in both partial positions")
+
+
+def test_plan_from_another_geometry_is_refused():
+    """A plan carries a key of its host-side geometry: a run with other head
+    counts that give the same tile shape (8/2 against 32/8 heads, both four
+    query heads per KV head) or another row total refuses it, writes
+    nothing and sets the plan error bit.  Neither geometry splits its keys,
+    so no run could write partials even if it accepted the plan."""
+    t = torch()
+    rng = np.random.default_rng(620)
+    nseg = 40
+    uq = rng.integers(0, 257, nseg)
+    uk = rng.integers(0, 257, nseg)
+    g_small = W.make_geometry([256] * nseg, [256] * nseg, uq, uk, 8, 2, 128, True,
+                              dtype=W.BF16)
+    g_big = W.make_geometry([256] * nseg, [256] * nseg, uq, uk, 32, 8, 128, True,
+                            dtype=W.BF16)
+    q, k, v = W.fill_qkv(g_big, 621)
+    wl = W.Workload("plan_key", 621, g_big, q, k, v)
+    dc = DeviceCase(wl)
+    n_ws = max(B.gvattn_fwd_workspace_size(nseg, g.total_q, g.hq, g.hkv, 128, B.GVATTN_BF16)
+               for g in (g_small, g_big))
+    ws = t.zeros(n_ws + 4096, dtype=t.uint8, device="cuda")
+    B.gvattn_fwd_plan(B.GVATTN_BF16, dc.cu_q, i32(g_small.cu_k), dc.used_q, i32(g_small.used_k),
+                      g_small.total_q, g_small.total_k, g_small.hq, g_small.hkv, 128, True,
+                      workspace=ws)
+    out, lse, _ = dc.fwd(fn=B.gvattn_fwd_run, workspace=ws)
+    assert B.gvattn_read_device_error(ws) & B.GVATTN_DEVERR_PLAN
+    assert max_split(ws) == 1
+    assert (out.float() == W.SENTINEL).all().item() and (lse == W.SENTINEL).all().item()
+    # same heads, one more block of gap rows at the end of Q / O: another total_q
+    B.gvattn_fwd_plan(B.GVATTN_BF16, dc.cu_q, i32(g_big.cu_k), dc.used_q, i32(g_big.used_k),
+                      g_big.total_q, g_big.total_k, g_big.hq, g_big.hkv, 128, True, workspace=ws)
+    q2 = t.cat([dc.q, dc.q[:64]])
+    out2 = t.full((g_big.total_q + 64, g_big.hq, 128), W.SENTINEL, dtype=t.bfloat16,
+                  device="cuda")
+    lse2 = t.full((g_big.hq, g_big.total_q + 64), W.SENTINEL, dtype=t.float32, device="cuda")
+    B.gvattn_fwd_run(q2, dc.k, dc.v, dc.cu_q, i32(g_big.cu_k), dc.used_q, i32(g_big.used_k),
+                     out2, lse2, float(g_big.scale), True, ws)
+    assert B.gvattn_read_device_error(ws) & B.GVATTN_DEVERR_PLAN
+    assert (out2.float() == W.SENTINEL).all().item() and (lse2 == W.SENTINEL).all().item()
+    # the matching plan still runs
+    out3, lse3, _ = dc.fwd(fn=B.gvattn_fwd_run, workspace=ws)
+    torch().cuda.synchronize()
+    assert not (out3.float() == W.SENTINEL).all().item()
+
+
 # --- split-K (few query tiles, long keys) ----------------------------------------
 
 def max_split(ws) -> int:

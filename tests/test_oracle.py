@@ -407,6 +407,58 @@ def test_merge_closed_form_two_parts():
     assert np.all(om == 0.0) and lm[0, 0] == -np.inf
 
 
+def _merge_scalar(lses, outs):
+    """The merge formula for one (row, head), in Python floats with exact
+    sums: m = max, w_p = e^(L_p - m), LSE = m + ln sum w, O = sum w_p O_p / W."""
+    m = max(lses)
+    if m == -math.inf:
+        return [0.0] * len(outs[0]), -math.inf
+    w = [math.exp(x - m) for x in lses]
+    W_ = math.fsum(w)
+    o = [math.fsum(wp * op[i] for wp, op in zip(w, outs)) / W_ for i in range(len(outs[0]))]
+    return o, m + math.log(W_)
+
+
+@pytest.mark.parametrize("nan_part", [0, 1, 2])
+def test_merge_nan_propagates(nan_part):
+    """A NaN LSE in one partial makes exactly that (row, head) NaN in O and
+    LSE, whichever partial holds it (a max that skips NaN, or keeps it only
+    in first position, fails one of the three placements); every other used
+    (row, head) equals the merge formula evaluated in exact sums, and gap
+    rows keep their values (the merge of visibility partitions, PR #312,
+    "Problem and behavior", with IEEE NaN propagation as the convention)."""
+    rng = np.random.default_rng(77 + nan_part)
+    cu_q, used_q = [0, 5, 9, 14], [4, 0, 3]
+    tq, hq, dv, nparts = 14, 3, 4, 3
+    outs = [rng.standard_normal((tq, hq, dv)) for _ in range(nparts)]
+    lses = [rng.standard_normal((hq, tq)) * 3.0 for _ in range(nparts)]
+    lses[1][0, 2] = -np.inf           # one partial without keys for a row
+    for p in range(nparts):
+        lses[p][2, 10] = -np.inf      # a (row, head) no partial saw a key for
+    nan_at = [(1, 0), (9, 2)]         # (row, head) pairs that get a NaN LSE
+    for r, h in nan_at:
+        lses[nan_part][h, r] = np.nan
+    o_init = np.full((tq, hq, dv), W.SENTINEL)
+    l_init = np.full((hq, tq), W.SENTINEL)
+    om, lm = oracle.lse_merge(outs, lses, cu_q, used_q, o_init, l_init)
+    for s in range(len(used_q)):
+        for r in range(cu_q[s], cu_q[s + 1]):
+            for h in range(hq):
+                if r >= cu_q[s] + used_q[s]:
+                    assert np.all(om[r, h] == W.SENTINEL) and lm[h, r] == W.SENTINEL
+                elif (r, h) in nan_at:
+                    assert np.all(np.isnan(om[r, h])) and np.isnan(lm[h, r])
+                else:
+                    o_want, l_want = _merge_scalar([float(x[h, r]) for x in lses],
+                                                   [x[r, h] for x in outs])
+                    assert not np.isnan(lm[h, r]) and not np.isnan(om[r, h]).any()
+                    if l_want == -math.inf:
+                        assert lm[h, r] == -np.inf and np.all(om[r, h] == 0.0)
+                    else:
+                        assert abs(lm[h, r] - l_want) < 1e-12
+                        assert np.max(np.abs(om[r, h] - o_want)) < 1e-12
+
+
 def test_flop_count_fp32_three_segments():
     g = W.fp32_three_segments().geom
     assert oracle.attention_flops(g.used_q, g.used_k, g.hq, g.d, g.dv, False) == 5_799_936
@@ -415,7 +467,7 @@ def test_flop_count_fp32_three_segments():
     assert oracle.attention_flops([5], [3], 1, 1, 1, True) == 6 * 4
 
 
-# --- key ranges (issue #18687, "Suggested fix" item 1) -------------------------
+# --- key ranges (issue #18687, "additional notes", possible fix 1) -------------------------
 
 def brute_force_ranges(q, k, v, cu_q, used_q, kr_off, kr_start, kr_len, scale, causal,
                        sentinel):
