@@ -22,7 +22,7 @@ What it computes (the sources are the pages' own statements of the method):
 * The gradients (``attention_bwd``): the pages' path is forward-only (PR
   #302 makes the backward raise); the backward here is the calculus of the
   forward above, written out.
-* TensorRT-LLM issue #18687, "Suggested fix" item 1: after the Ulysses
+* TensorRT-LLM issue #18687, "additional notes", possible fix 1: after the Ulysses
   all-to-all the keys arrive rank-major, so a sample's valid keys are several
   runs of rows rather than one prefix.  ``attention_fwd_ranges`` takes each
   segment's keys as an ordered list of row ranges.
@@ -179,7 +179,7 @@ def segment_key_rows(kr_off, kr_start, kr_len, s: int) -> np.ndarray:
 def attention_fwd_ranges(q, k, v, cu_q, used_q, kr_off, kr_start, kr_len, scale, causal,
                          out_init=None, lse_init=None, workers: int | None = None):
     """Whole-launch oracle when every segment's keys are a list of row ranges
-    (issue #18687, "Suggested fix" item 1).  The segment's key sequence is the
+    (issue #18687, "additional notes", possible fix 1).  The segment's key sequence is the
     concatenation of its ranges; with it gathered, the computation is the one
     of ``attention_fwd`` with used_k = the total length (causal alignment is
     bottom-right over that sequence)."""

@@ -287,7 +287,7 @@ def ulysses_joint(seed: int = 6, ranks: int = 2, text_cap: int = 4096, video: in
                   text_lens=(24, 700), nq: int = 4096, hq: int = 32, hkv: int = 8,
                   d: int = 128, dtype: str = BF16) -> Workload:
     """CFG batch of 2 under Ulysses sequence parallelism (issue #18687,
-    "Suggested fix" item 1): each sample's keys arrive rank-major, rank r
+    "additional notes", possible fix 1): each sample's keys arrive rank-major, rank r
     holding text rows [r*T/R, (r+1)*T/R) of the padded text and video rows
     [r*V/R, (r+1)*V/R).  The valid keys of sample b are, per rank, the real
     text rows of that chunk (text_lens[b] in total, pad slots exactly zero)

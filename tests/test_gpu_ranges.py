@@ -2,8 +2,8 @@
 oracle's range form, through the C ABI.
 
 Segment keys given as ordered lists of K/V row ranges: the rank-major key
-order after a Ulysses all-to-all (TensorRT-LLM issue #18687, "Suggested fix"
-item 1), random ranges (empty, overlapping, out of order, none), one range
+order after a Ulysses all-to-all (TensorRT-LLM issue #18687, "additional
+notes", possible fix 1), random ranges (empty, overlapping, out of order, none), one range
 per segment (must equal the prefix form bit for bit) and the two visibility
 partitions of the multiview workload fused into one launch.
 """
