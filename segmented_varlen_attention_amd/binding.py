@@ -64,12 +64,25 @@ SIGNATURES = {
 }
 
 
+def _bind_torch_runtime() -> None:
+    """PyTorch ships its own HIP runtime (libamdhip64.so.7 in torch/lib).
+    Importing torch before the library is opened makes the library bind to
+    that runtime (same soname, already loaded) instead of loading the
+    system copy next to it: two HIP runtimes in one process see the GPU
+    inconsistently, and the second one to start can report no device."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # a process without torch uses the system runtime alone
+        pass
+
+
 def load_library(path: str | None = None) -> ctypes.CDLL:
     """Load libgvattn.so (once) and declare the C signatures."""
     global _lib
     with _lock:
         if _lib is not None and path is None:
             return _lib
+        _bind_torch_runtime()
         p = path or os.environ.get("GVATTN_LIBRARY") or LIB_PATH
         if not os.path.exists(p):
             raise RuntimeError(

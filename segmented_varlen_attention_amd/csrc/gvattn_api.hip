@@ -3,6 +3,9 @@
 // validation paths run (and are tested) on machines without a GPU.
 #include <math.h>
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include <mutex>
 #include <unordered_map>
 
@@ -62,6 +65,15 @@ int device_cu_count() {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// GVATTN_ERR_HIP for a failed runtime call; with GVATTN_DEBUG set in the
+// environment the HIP error and the step are also printed to stderr.
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return GVATTN_OK;
+  static const bool debug = getenv("GVATTN_DEBUG") != nullptr;
+  if (debug) fprintf(stderr, "gvattn: %s: %s (%d)\n", where, hipGetErrorString(e), (int)e);
+  return GVATTN_ERR_HIP;
+}
 
 bool dtype_ok(int32_t dtype) {
   return dtype == GVATTN_FP32 || dtype == GVATTN_BF16 || dtype == GVATTN_FP16;
@@ -138,9 +150,8 @@ Geometry make_geom(const int32_t* cu_q, const int32_t* cu_k, const int32_t* used
   return g;
 }
 
-int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
+int do_plan(int32_t dtype, const Geometry& g, const WsLayout& L, void* ws, hipStream_t stream) {
   const TileShape t = choose_shape(dtype, g.hq, g.hkv, g.d);
-  const WsLayout L = layout_of(dtype, g.nseg, g.total_q, g.hq, g.hkv, g.d, g.dv);
   PlanArgs a;
   a.g = g;
   a.ws = view_workspace(ws, L);
@@ -154,13 +165,12 @@ int do_plan(int32_t dtype, const Geometry& g, void* ws, hipStream_t stream) {
   const int dmax = g.d > g.dv ? g.d : g.dv;
   a.q_row_bytes = (int64_t)g.hq * dmax * esize(dtype);
   a.k_row_bytes = (int64_t)g.hkv * dmax * esize(dtype);
-  return launch_plan(a, stream) == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
+  return hip_status(launch_plan(a, stream), "plan");
 }
 
-int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const void* v,
-           float scale, void* out, float* lse, void* ws, hipStream_t stream) {
+int do_run(int32_t dtype, const Geometry& g, const WsLayout& L, const void* q, const void* k,
+           const void* v, float scale, void* out, float* lse, void* ws, hipStream_t stream) {
   const TileShape t = choose_shape(dtype, g.hq, g.hkv, g.d);
-  const WsLayout L = layout_of(dtype, g.nseg, g.total_q, g.hq, g.hkv, g.d, g.dv);
   FwdArgs a;
   a.g = g;
   a.ws = view_workspace(ws, L);
@@ -178,7 +188,7 @@ int do_run(int32_t dtype, const Geometry& g, const void* q, const void* k, const
                                         : launch_fwd_fp32(a, t, max_work, stream, &ok);
   if (!ok) return GVATTN_ERR_UNSUPPORTED;
   if (e == hipSuccess && L.splits > 1) e = launch_split_merge(a, dtype, stream);
-  return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
+  return hip_status(e, "forward");
 }
 
 int check_fwd_args(int32_t dtype, const void* q, const void* k, const void* v,
@@ -242,8 +252,9 @@ int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   pk.max_tiles = (int32_t)L.k.max_tiles;
   pk.n_head_chunks = g.hkv;
   pk.key = geometry_key(kBwdKeyRows, g, L.k, kPlanBwdK);
-  if (launch_plan(pq, stream) != hipSuccess) return GVATTN_ERR_HIP;
-  if (launch_plan(pk, stream) != hipSuccess) return GVATTN_ERR_HIP;
+  int rc = hip_status(launch_plan(pq, stream), "backward query plan");
+  if (rc == GVATTN_OK) rc = hip_status(launch_plan(pk, stream), "backward key plan");
+  if (rc != GVATTN_OK) return rc;
 
   BwdArgs b;
   b.g = g;
@@ -270,7 +281,7 @@ int do_bwd(int32_t dtype, const Geometry& g, const void* q, const void* k, const
   bool ok = false;
   const hipError_t e = launch_bwd(b, dtype, t, stream, &ok);
   if (!ok) return GVATTN_ERR_UNSUPPORTED;
-  return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
+  return hip_status(e, "backward");
 }
 
 }  // namespace
@@ -300,7 +311,8 @@ int gvattn_fwd_plan(int32_t dtype, const int32_t* cu_q, const int32_t* cu_k,
   if (rc != GVATTN_OK) return rc;
   const Geometry g =
       make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
-  return do_plan(dtype, g, workspace, static_cast<hipStream_t>(hip_stream));
+  return do_plan(dtype, g, layout_of(dtype, nseg, total_q, hq, hkv, d, d_v), workspace,
+                 static_cast<hipStream_t>(hip_stream));
 }
 
 int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
@@ -316,8 +328,8 @@ int gvattn_fwd_run(int32_t dtype, const void* q, const void* k, const void* v,
   if (rc != GVATTN_OK || nseg == 0) return rc;
   const Geometry g =
       make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
-  return do_run(dtype, g, q, k, v, softmax_scale, out, lse, workspace,
-                static_cast<hipStream_t>(hip_stream));
+  return do_run(dtype, g, layout_of(dtype, nseg, total_q, hq, hkv, d, d_v), q, k, v,
+                softmax_scale, out, lse, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
 int gvattn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
@@ -334,9 +346,10 @@ int gvattn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
   const Geometry g =
       make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  rc = do_plan(dtype, g, workspace, s);
+  const WsLayout L = layout_of(dtype, nseg, total_q, hq, hkv, d, d_v);
+  rc = do_plan(dtype, g, L, workspace, s);
   if (rc != GVATTN_OK) return rc;
-  return do_run(dtype, g, q, k, v, softmax_scale, out, lse, workspace, s);
+  return do_run(dtype, g, L, q, k, v, softmax_scale, out, lse, workspace, s);
 }
 
 int gvattn_fwd_ranges(int32_t dtype, const void* q, const void* k, const void* v,
@@ -363,9 +376,10 @@ int gvattn_fwd_ranges(int32_t dtype, const void* q, const void* k, const void* v
   g.kr_len = kr_len;
   g.nranges = nranges;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  rc = do_plan(dtype, g, workspace, s);
+  const WsLayout L = layout_of(dtype, nseg, total_q, hq, hkv, d, d_v);
+  rc = do_plan(dtype, g, L, workspace, s);
   if (rc != GVATTN_OK) return rc;
-  return do_run(dtype, g, q, k, v, softmax_scale, out, lse, workspace, s);
+  return do_run(dtype, g, L, q, k, v, softmax_scale, out, lse, workspace, s);
 }
 
 int gvattn_lse_merge(int32_t nparts, const void* const* part_out, const float* const* part_lse,
@@ -404,7 +418,7 @@ int gvattn_lse_merge(int32_t nparts, const void* const* part_out, const float* c
   bool ok = false;
   hipError_t e = launch_merge(a, part_dtype, out_dtype, static_cast<hipStream_t>(hip_stream), &ok);
   if (!ok) return GVATTN_ERR_UNSUPPORTED;
-  return e == hipSuccess ? GVATTN_OK : GVATTN_ERR_HIP;
+  return hip_status(e, "merge");
 }
 
 size_t gvattn_bwd_workspace_size(int32_t nseg, int32_t total_q, int32_t total_k, int32_t hq,

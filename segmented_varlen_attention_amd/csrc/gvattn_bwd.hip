@@ -710,8 +710,7 @@ hipError_t launch_persistent(K kern, int threads, int64_t max_work, const BwdArg
                              hipStream_t s) {
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), threads, max_work);
   if (grid <= 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(grid), dim3(threads), s, a);
 }
 
 template <typename T, int D, int DV>
@@ -736,8 +735,7 @@ hipError_t launch_dims(const BwdArgs& a, const TileShape& t, hipStream_t s, bool
   const int grid = (int)(r_work < 2048 ? r_work : 2048);
   if (grid > 0) {
     auto reduce = bwd_kv_reduce_kernel<T, D, DV>;
-    hipLaunchKernelGGL(reduce, dim3(grid), dim3(256), 0, s, a);
-    e = hipGetLastError();
+    e = launch_kernel(reduce, dim3(grid), dim3(256), s, a);
   }
   return e;
 }

@@ -99,8 +99,7 @@ hipError_t launch_d(const FwdArgs& a, const TileShape& t, int64_t max_work, hipS
   auto kern = fwd_fp32_kernel<DQ, DV>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), kThreads, max_work);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, t.rows);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(grid), dim3(kThreads), s, a, t.rows);
 }
 
 template <int DQ>

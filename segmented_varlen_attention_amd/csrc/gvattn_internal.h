@@ -304,6 +304,17 @@ struct MergeArgs {
   int32_t* err;
 };
 
+// Launches `kern` and returns the status of this launch itself, never an
+// error some earlier runtime call of other code left in this thread's
+// last-error slot (hipLaunchKernelGGL + hipGetLastError would report that).
+template <typename T> struct NoDeduce { using type = T; };
+template <typename... P>
+inline hipError_t launch_kernel(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t s,
+                                typename NoDeduce<P>::type... args) {
+  void* ptrs[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, 0, s);
+}
+
 // Host-side launchers (one translation unit each).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // Combines the split-K partials of the segments the plan split (dtype of

@@ -239,11 +239,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 }
 
 template <typename TIn, typename TOut, int D>
-void launch_np(const MergeArgs& a, int grid, hipStream_t s) {
+hipError_t launch_np(const MergeArgs& a, int grid, hipStream_t s) {
   if (a.nparts == 2)
-    hipLaunchKernelGGL((merge_kernel<TIn, TOut, D, 2>), dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((merge_kernel<TIn, TOut, D, 0>), dim3(grid), dim3(kThreads), 0, s, a);
+    return launch_kernel(merge_kernel<TIn, TOut, D, 2>, dim3(grid), dim3(kThreads), s, a);
+  return launch_kernel(merge_kernel<TIn, TOut, D, 0>, dim3(grid), dim3(kThreads), s, a);
 }
 
 template <typename TIn, typename TOut>
@@ -259,11 +258,10 @@ hipError_t launch_t(const MergeArgs& a, hipStream_t s, bool* ok) {
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int grid = (int)blocks;
   switch (a.d) {
-    case 64: launch_np<TIn, TOut, 64>(a, grid, s); break;
-    case 128: launch_np<TIn, TOut, 128>(a, grid, s); break;
-    default: launch_np<TIn, TOut, 256>(a, grid, s); break;
+    case 64: return launch_np<TIn, TOut, 64>(a, grid, s);
+    case 128: return launch_np<TIn, TOut, 128>(a, grid, s);
+    default: return launch_np<TIn, TOut, 256>(a, grid, s);
   }
-  return hipGetLastError();
 }
 
 // Split-K merge: for every used row of a segment the plan split into S > 1
@@ -329,13 +327,13 @@ hipError_t launch_split_t(const FwdArgs& a, hipStream_t s) {
   const int64_t blocks = ((int64_t)a.g.hq * a.g.total_q + per_block - 1) / per_block;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(kThreads);
   switch (a.g.dv) {
-    case 64: hipLaunchKernelGGL((split_merge_kernel<TOut, 64>), dim3((int)blocks), dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((split_merge_kernel<TOut, 128>), dim3((int)blocks), dim3(kThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((split_merge_kernel<TOut, 256>), dim3((int)blocks), dim3(kThreads), 0, s, a); break;
+    case 64: return launch_kernel(split_merge_kernel<TOut, 64>, grid, block, s, a);
+    case 128: return launch_kernel(split_merge_kernel<TOut, 128>, grid, block, s, a);
+    case 256: return launch_kernel(split_merge_kernel<TOut, 256>, grid, block, s, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
