@@ -26,7 +26,14 @@
 //     transpose per 16 lanes), so V is never transposed in memory.
 //   * Online softmax in the exp2 domain with FP32 max/sum.  The running max
 //     is only raised (and O rescaled) when a row's max grows by more than
-//     2^8, which keeps the rescale off the common path.
+//     2^8, which keeps the rescale off the common path.  Two row sums are
+//     kept: the sum of the FP32 weights gives the LSE, the sum of the
+//     weights as rounded for the P.V product normalises O, so that O is a
+//     weighted mean of V whose weights' rounding largely cancels (a key that
+//     dominates a row then costs no rounding error; with the max held back,
+//     its weight is not exactly 1).
+//   * Rows that see at most one tile of keys add the rounding remainder of
+//     P as a second product on that tile.
 //   * Buffer resources end at the segment's last used row: loads past it
 //     return zero (ragged key tiles, gap rows, buffer ends) and stores past
 //     it are dropped (gap rows of O stay bit-exact).  Key-padding and causal
@@ -271,6 +278,7 @@ void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < C::DB; ++i) o[i] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
+    float lh_run = 0.f;  // sum of the rounded weights (normalises O)
 
     const int row = wr0 + r32;                       // this lane's query row
     const int lim = a.g.causal ? min(uk, row + uk - uq + 1) : uk;
@@ -363,6 +371,7 @@ void fwd_mfma_kernel(FwdArgs a) {
           const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
           m_run = m_new;
           l_run *= alpha;
+          lh_run *= alpha;
 #pragma unroll
           for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
         }
@@ -444,6 +453,7 @@ void fwd_mfma_kernel(FwdArgs a) {
             const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
+            lh_run *= alpha;
 #pragma unroll
             for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
           }
@@ -469,25 +479,52 @@ void fwd_mfma_kernel(FwdArgs a) {
         for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
           for (int j = 0; j < 8; ++j) pb[kb][a2][j] = (T)s[kb][8 * a2 + j];
+#pragma unroll
+      for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) lh_run = E::sum8(pb[kb][a2], lh_run);
 
       // O^T += V^T . P^T, V^T read transposed from the row-major V tile
+      auto pv = [&](const v8 (&p)[C::NKB_][2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const int dcol = db * 32 + vd_l;
-        const int ch = dcol >> 3, within = (dcol & 7) * 2;
+        for (int db = 0; db < C::DB; ++db) {
+          const int dcol = db * 32 + vd_l;
+          const int ch = dcol >> 3, within = (dcol & 7) * 2;
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2) {
+              const int r_lo = kb * 32 + a2 * 16 + vrow_l;
+              const int r_hi = r_lo + 8;
+              const i16x4 lo = read_tr(Vs + r_lo * (DV * 2) + ((ch ^ swz_v<DV>(r_lo)) << 4) + within);
+              const i16x4 hi = read_tr(Vs + r_hi * (DV * 2) + ((ch ^ swz_v<DV>(r_hi)) << 4) + within);
+              const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+              const v8 va = __builtin_bit_cast(v8, both);
+              o[db] = E::mfma(va, p[kb][a2], o[db]);
+            }
+        }
+      };
+      // Rows that see at most one tile of keys in all: the rounding of their
+      // few large weights to 16 bits would dominate their error, so the
+      // tiles holding their keys also add the rounding remainder of P,
+      // P - round(P), as a second product (P is then exact to about 2^-17).
+      if (kbase < C::BN && lim_wt <= C::BN) {
+        keep_branch();
+        v8 pl[C::NKB_][2];
 #pragma unroll
         for (int kb = 0; kb < C::NKB_; ++kb)
 #pragma unroll
-          for (int a2 = 0; a2 < 2; ++a2) {
-            const int r_lo = kb * 32 + a2 * 16 + vrow_l;
-            const int r_hi = r_lo + 8;
-            const i16x4 lo = read_tr(Vs + r_lo * (DV * 2) + ((ch ^ swz_v<DV>(r_lo)) << 4) + within);
-            const i16x4 hi = read_tr(Vs + r_hi * (DV * 2) + ((ch ^ swz_v<DV>(r_hi)) << 4) + within);
-            const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            const v8 va = __builtin_bit_cast(v8, both);
-            o[db] = E::mfma(va, pb[kb][a2], o[db]);
-          }
+          for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              pl[kb][a2][j] = (T)(s[kb][8 * a2 + j] - (float)pb[kb][a2][j]);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+          for (int a2 = 0; a2 < 2; ++a2) lh_run = E::sum8(pl[kb][a2], lh_run);
+        pv(pl);
       }
+      pv(pb);
       if constexpr (KR) cur = nx;
     };
     if constexpr (C::MIN_BLOCKS > 1) {
@@ -505,8 +542,9 @@ void fwd_mfma_kernel(FwdArgs a) {
 
     // epilogue: normalise, LSE, stage O through LDS, full-row stores
     const float l_tot = sum_across_halves(l_run);
+    const float lh_tot = sum_across_halves(lh_run);
     const bool dead = (l_tot == 0.f);
-    const float inv = dead ? 0.f : 1.f / l_tot;
+    const float inv = dead ? 0.f : 1.f / lh_tot;
     const float lse = dead ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
     if (partial) {
       // split-K chunk: FP32 O (normalised over the chunk) and LSE of chunk
@@ -569,8 +607,7 @@ hipError_t launch_one(const FwdArgs& a, int64_t max_work, hipStream_t s) {
   FwdArgs args = a;
   args.n_cu = device_cu_count();
   if (args.n_cu <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, s, args);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(grid), dim3(C::NT), s, args);
 }
 
 template <typename T, int DQ, int DV>

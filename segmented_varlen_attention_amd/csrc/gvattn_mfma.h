@@ -17,11 +17,22 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 // Element type of Q/K/V/O: the matrix-core instruction and the rounding
 // conversions (round to nearest even) for P and O.
 template <typename T> struct Elem;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 template <> struct Elem<__bf16> {
   using v8 = bf16x8;
   using v4 = bf16x4;
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // acc + the sum of the eight 16-bit values (v_dot2 with ones, FP32 sum)
+  static __device__ __forceinline__ float sum8(v8 p, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
   }
 };
 template <> struct Elem<_Float16> {
@@ -29,6 +40,13 @@ template <> struct Elem<_Float16> {
   using v4 = f16x4;
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float sum8(v8 p, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
   }
 };
 typedef short i16x8 __attribute__((ext_vector_type(8)));

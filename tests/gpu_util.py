@@ -146,12 +146,17 @@ def compare(o_gpu, l_gpu, o_ref, l_ref, dtype: str, where: str = "", o_abs=None,
     fin = ~dead
     lse_err = float(np.max(np.abs(l_gpu[fin] - l_ref[fin]), initial=0.0))
     err = np.abs(o_gpu.astype(np.float64) - o_ref)
-    stats = {"lse_err": lse_err, "out_err": float(err.max(initial=0.0))}
+    stats = {"lse_err": lse_err, "out_err": float(err.max(initial=0.0)),
+             "n_elems": int(err.size), "n_over_5e-3": int(np.count_nonzero(err > 5e-3))}
     if bf16:
         floor = np.abs(out_round(dtype, o_ref) - o_ref)
         ex = err - floor
         excess = float(np.max(ex, initial=0.0))
         stats.update(out_excess=excess, floor=float(floor.max(initial=0.0)))
+        if ex.size:
+            i = np.unravel_index(int(np.argmax(ex)), ex.shape)
+            stats["worst"] = {"index": [int(x) for x in i], "gpu": float(o_gpu[i]),
+                              "ref": float(o_ref[i]), "floor": float(floor[i])}
         flat = TOL_OUT[dtype] if tol_out is None else tol_out
         if o_abs is None:
             assert excess <= flat, f"{where}: {dtype} output error beyond rounding {excess:.3g} ({stats})"
@@ -166,6 +171,47 @@ def compare(o_gpu, l_gpu, o_ref, l_ref, dtype: str, where: str = "", o_abs=None,
     assert lse_err <= TOL_LSE, f"{where}: LSE error {stats}"
     assert np.isfinite(o_gpu).all(), f"{where}: non-finite output"
     return stats
+
+
+def tile_rows(uq: int) -> np.ndarray:
+    """Whole 32-row tiles at the start, middle and end of a segment's used
+    rows (fewer rows when the segment is shorter)."""
+    if uq <= 0:
+        return np.zeros(0, np.int64)
+    mid = max(0, min(uq - 32, uq // 2 - 16))
+    parts = [np.arange(0, min(32, uq)), np.arange(mid, min(uq, mid + 32)),
+             np.arange(max(0, uq - 32), uq)]
+    return np.unique(np.concatenate(parts)).astype(np.int64)
+
+
+def oracle_rows_many(wl, geom, samples, workers: int = 16):
+    """oracle_rows for many (segment, rows) samples at once, on a thread
+    pool over (sample, head) items with single-threaded BLAS per worker.
+    Returns a list of (O [n, hq, dv], LSE [hq, n]) in sample order."""
+    import concurrent.futures as cf
+    g = geom
+    grp = g.hq // g.hkv
+    res = [(np.zeros((len(r), g.hq, g.dv)), np.zeros((g.hq, len(r)))) for _, r in samples]
+
+    def run(item):
+        i, h = item
+        seg, rows = samples[i]
+        oh, lh = oracle.segment_head_rows(wl.q, wl.k, wl.v, int(g.cu_q[seg]), int(g.cu_k[seg]),
+                                          int(g.used_q[seg]), int(g.used_k[seg]), h, h // grp,
+                                          float(g.scale), g.causal, np.asarray(rows, np.int64))
+        res[i][0][:, h, :] = oh
+        res[i][1][h, :] = lh
+
+    items = [(i, h) for i in range(len(samples)) for h in range(g.hq)]
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        import contextlib
+        ctx = contextlib.nullcontext()
+    with ctx, cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(run, items))
+    return res
 
 
 def oracle_rows(wl, geom, seg: int, rows: np.ndarray):
@@ -198,28 +244,43 @@ def compare_full(out, lse, wl, geom=None, o_ref=None, l_ref=None, where="", deri
     g = geom or wl.geom
     if o_ref is None:
         o_ref, l_ref = oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k,
-                                            float(g.scale), g.causal, workers=8)
+                                            float(g.scale), g.causal, workers=16)
     check_gap_rows(out, lse, g)
     m = used_row_mask(g)
     o_gpu, l_gpu = to_np(out), to_np(lse)
     o_abs = oracle_abs(wl, g)[m] if (derived and g.dtype != W.FP32) else None
-    return compare(o_gpu[m], l_gpu[:, m], o_ref[m], l_ref[:, m], g.dtype, where,
-                   o_abs=o_abs)
+    st = compare(o_gpu[m], l_gpu[:, m], o_ref[m], l_ref[:, m], g.dtype, where, o_abs=o_abs)
+    if "worst" in st:  # the worst element's global row
+        st["worst"]["index"][0] = int(np.nonzero(m)[0][st["worst"]["index"][0]])
+    return st
+
+
+def merge_stats(stats):
+    """Maxima of per-sample stats (element counts are summed)."""
+    if not stats:
+        return {}
+    out = {}
+    for k in stats[0]:
+        if k == "worst":
+            continue
+        vals = [s[k] for s in stats if k in s]
+        out[k] = sum(vals) if k.startswith("n_") else max(vals)
+    if "out_excess" in out:
+        out["worst"] = max(stats, key=lambda s: s.get("out_excess", 0.0)).get("worst")
+    return out
 
 
 def compare_sampled(out, lse, wl, samples, geom=None, where=""):
     """samples: list of (segment, row indices within the segment)."""
     g = geom or wl.geom
     check_gap_rows(out, lse, g)
+    samples = [(seg, np.asarray(rows, np.int64)) for seg, rows in samples if len(rows) > 0]
+    refs = oracle_rows_many(wl, g, samples)
     stats = []
-    for seg, rows in samples:
-        rows = np.asarray(rows, np.int64)
-        if len(rows) == 0:
-            continue
-        o_ref, l_ref = oracle_rows(wl, g, seg, rows)
+    for (seg, rows), (o_ref, l_ref) in zip(samples, refs):
         gi = torch().from_numpy(g.cu_q[seg] + rows).to("cuda")
         o_gpu = to_np(out.index_select(0, gi))
         l_gpu = to_np(lse.index_select(1, gi))
         stats.append(compare(o_gpu, l_gpu, o_ref, l_ref, g.dtype,
                              f"{where} seg {seg}"))
-    return {k: max(s[k] for s in stats) for k in stats[0]} if stats else {}
+    return merge_stats(stats)

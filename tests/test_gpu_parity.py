@@ -14,7 +14,7 @@ from segmented_varlen_attention_amd import binding as B
 from segmented_varlen_attention_amd import workloads as W
 
 from gpu_util import (DeviceCase, check_gap_rows, compare, compare_full, compare_sampled, i32,
-                      oracle_abs, say, to_np, torch, used_row_mask)
+                      oracle_abs, say, tile_rows, to_np, torch, used_row_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -175,16 +175,14 @@ def test_cfg_cross_attention():
 
 
 def test_causal_replay_64x2048():
+    """Every used row of all 64 segments against the full oracle, plus the
+    rows with no visible key checked on the device."""
     wl = W.causal_replay()
     g = wl.geom
     out, lse, ws = DeviceCase(wl).fwd()
     assert B.gvattn_read_device_error(ws) == 0
-    empty = [int(s) for s in np.where(g.used_k == 0)[0]]
-    big = [int(s) for s in np.argsort(-(g.used_q.astype(np.int64) * g.used_k))[:3]]
-    more = [s for s in (5, 17, 33, 48, 63) if s not in big + empty]
-    samples = [(s, np.arange(g.used_q[s])) for s in empty + big + more]
-    st = compare_sampled(out, lse, wl, samples, where="causal_replay")
-    say("[causal_replay]", st)
+    st = compare_full(out, lse, wl, where="causal_replay")
+    say("[causal_replay] all used rows", st)
     # any size: all used rows finite; rows with no visible key exactly (0, -inf)
     m = used_row_mask(g)
     t = torch()
@@ -201,6 +199,12 @@ def test_causal_replay_64x2048():
 
 
 def test_multiview_partitions_merge():
+    """Both partitions, their merge and the single pass, each on whole
+    32-row tiles at the start, middle and end of every segment against the
+    oracle.  On the device, the merged result is compared with the single
+    pass on every row: each of the two is within the output-rounding floor
+    plus 5e-3 of the exact result, so they differ by at most twice that
+    (|O| < 4 here, so the floor is at most 2^-7)."""
     wl = W.multiview_partitions()
     g = wl.geom
     dc = DeviceCase(wl)
@@ -215,34 +219,26 @@ def test_multiview_partitions_merge():
                        device_error=err)
     torch().cuda.synchronize()
     assert int(err.item()) == 0
-    rng = np.random.default_rng(44)
-    samples = [(s, np.sort(rng.choice(8190, 12, replace=False))) for s in range(8)]
-    samples[0] = (0, np.array([0, 1, 8188, 8189]))
+    samples = [(s, tile_rows(int(g.used_q[s]))) for s in range(g.nseg)]
     st_m = compare_sampled(out_m, lse_m, wl, samples, where="multiview_partitions merged")
     st_s = compare_sampled(out_s, lse_s, wl, samples, where="multiview_partitions single")
     say("[multiview_partitions] merged", st_m, "single", st_s)
-    # partitions against their own oracle
-    st_a = compare_sampled(out_a, lse_a, wl, samples[:3], geom=ga, where="multiview_partitions A")
-    say("[multiview_partitions] A", st_a)
-    # merged vs single pass on the device, all rows
-    t = torch()
+    st_a = compare_sampled(out_a, lse_a, wl, samples, geom=ga, where="multiview_partitions A")
+    st_b = compare_sampled(out_b, lse_b, wl, samples, geom=gb, where="multiview_partitions B")
+    say("[multiview_partitions] A", st_a, "B", st_b)
     d_lse = (lse_m - lse_s).abs().max().item()
     d_out = (out_m.float() - out_s.float()).abs().max().item()
     say(f"[multiview_partitions] merged-vs-single max |dLSE|={d_lse:.3g} max |dO|={d_out:.3g}")
-    assert d_lse <= 2e-5 and d_out <= 1.6e-2
+    assert d_lse <= 2e-5 and d_out <= 2 * (2.0 ** -7 + 5e-3)
 
 
 def test_large_head_d256():
+    """Whole 32-row tiles at the start, middle and end of all 16 segments."""
     wl = W.large_head_d256()
     g = wl.geom
     out, lse, ws = DeviceCase(wl).fwd()
     assert B.gvattn_read_device_error(ws) == 0
-    rng = np.random.default_rng(55)
-    samples = []
-    for s in range(g.nseg):
-        uq = int(g.used_q[s])
-        rows = np.unique(np.concatenate([[0, uq - 1], rng.choice(uq, 6, replace=False)]))
-        samples.append((s, rows))
+    samples = [(s, tile_rows(int(g.used_q[s]))) for s in range(g.nseg)]
     st = compare_sampled(out, lse, wl, samples, where="large_head_d256")
     say("[large_head_d256]", st)
 
