@@ -205,6 +205,32 @@ int gvattn_fwd_ranges(int32_t dtype, const void* q, const void* k, const void* v
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * gvattn_fwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * gvattn_fwd, minus `workspace` / `workspace_bytes`.  The plan (and any
+ * split-K partials) goes to a static device array of
+ * GVATTN_NOALLOC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends; nothing is allocated or freed.  When the
+ * ordinary split-K partials do not fit, fewer key chunks are used (same
+ * results within the stated tolerances); a geometry whose plan alone does
+ * not fit returns GVATTN_ERR_WORKSPACE before anything is enqueued.
+ * All calls on one device share the array: calls that may overlap on one
+ * device (different streams, or threads without ordering) race and must
+ * be serialised by the caller.  The array needs no clearing: every call
+ * writes the plan it reads.
+ */
+#define GVATTN_NOALLOC_SCRATCH_BYTES 33554432 /* 32 MiB */
+
+int gvattn_fwd_noalloc(int32_t dtype, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       const int32_t* seqused_q, const int32_t* seqused_k,
+                       int32_t nseg, int32_t total_q, int32_t total_k,
+                       int32_t hq, int32_t hkv, int32_t d, int32_t d_v,
+                       float softmax_scale, int32_t causal,
+                       void* out, float* lse, void* hip_stream);
+
+/*
  * FP32 LSE merge of nparts partial results over key partitions (PR #312,
  * "Problem and behavior").  For every used row (rows [cu_seqlens_q[s],
  * cu_seqlens_q[s] + seqused_q[s])) and head, in FP32:

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     gvattn_bwd_workspace_size,
     gvattn_fwd,
     gvattn_fwd_plan,
+    gvattn_fwd_noalloc,
     gvattn_fwd_ranges,
     gvattn_fwd_run,
     gvattn_fwd_workspace_size,

@@ -34,6 +34,7 @@ GVATTN_DEVERR_KRANGES = 32
 
 GVATTN_MAX_PARTS = 8
 GVATTN_WORKSPACE_ALIGN = 256
+GVATTN_NOALLOC_SCRATCH_BYTES = 33554432
 
 _lock = threading.Lock()
 _lib = None
@@ -49,6 +50,9 @@ SIGNATURES = {
     "gvattn_fwd_run": (ctypes.c_int, _FWD_ARGS),
     "gvattn_fwd_plan": (ctypes.c_int, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _vp, _sz, _vp]),
+    "gvattn_fwd_noalloc": (ctypes.c_int, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp,
+                                          _vp]),
     "gvattn_fwd_ranges": (ctypes.c_int, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                          _vp, _vp, _vp, _sz, _vp]),
@@ -216,6 +220,20 @@ def gvattn_fwd_run(q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, ou
     _need(workspace is not None, "gvattn_fwd_run needs the planned workspace")
     return _fwd_call("gvattn_fwd_run", q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q,
                      seqused_k, out, lse, softmax_scale, causal, workspace, stream)
+
+
+def gvattn_fwd_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, lse,
+                       softmax_scale, causal=False, stream=None) -> None:
+    """gvattn_fwd without a workspace: the library's static per-device
+    scratch holds the plan (calls that overlap on one device race)."""
+    nseg, total_q, total_k, hq, hkv, d, dv = _fwd_common(
+        q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, out, lse)
+    rc = load_library().gvattn_fwd_noalloc(
+        _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+        cu_seqlens_k.data_ptr(), seqused_q.data_ptr(), seqused_k.data_ptr(), nseg, total_q,
+        total_k, hq, hkv, d, dv, float(softmax_scale), int(bool(causal)), out.data_ptr(),
+        lse.data_ptr(), _stream_ptr(stream))
+    _check(rc, "gvattn_fwd_noalloc")
 
 
 def gvattn_fwd_ranges(q, k, v, cu_seqlens_q, seqused_q, kr_off, kr_start, kr_len, out, lse,

@@ -205,6 +205,50 @@ int check_fwd_args(int32_t dtype, const void* q, const void* k, const void* v,
   return check_workspace(ws, ws_bytes, layout_of(dtype, nseg, total_q, hq, hkv, d, dv));
 }
 
+// ---- allocation-free forward -------------------------------------------------
+
+// Device memory of gvattn_fwd_noalloc: the plan and any split-K partials.
+// Each device the library runs on holds its own copy until the process
+// ends.  Host code never uses this name as an address (on the host it is
+// only a stand-in); it uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[GVATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Address of the current device's scratch array, looked up once per device
+// (with that device current).
+hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// Workspace layout that fits the scratch array: the ordinary layout when it
+// fits, else the same with fewer split-K chunks.  bytes > the array's size
+// when even the plan alone does not fit.
+WsLayout noalloc_layout(int32_t dtype, int32_t nseg, int32_t total_q, int32_t hq, int32_t hkv,
+                        int32_t d, int32_t dv) {
+  const TileShape t = choose_shape(dtype, hq, hkv, d);
+  const int64_t cap = (int64_t)GVATTN_NOALLOC_SCRATCH_BYTES;
+  const int64_t per_split = (int64_t)total_q * hq * (dv + 1) * 4;
+  WsLayout L = ws_layout(nseg, total_q, hq, dv, t, dtype);
+  while ((int64_t)L.bytes > cap && L.splits > 1)  // one chunk fewer at a time
+    L = ws_layout(nseg, total_q, hq, dv, t, dtype, true, 1, (int64_t)(L.splits - 1) * per_split);
+  return L;
+}
+
 // ---- backward --------------------------------------------------------------
 
 constexpr int kPlanBwdQ = 1 << 20, kPlanBwdK = 2 << 20;  // plan-key flags
@@ -380,6 +424,30 @@ int gvattn_fwd_ranges(int32_t dtype, const void* q, const void* k, const void* v
   rc = do_plan(dtype, g, L, workspace, s);
   if (rc != GVATTN_OK) return rc;
   return do_run(dtype, g, L, q, k, v, softmax_scale, out, lse, workspace, s);
+}
+
+int gvattn_fwd_noalloc(int32_t dtype, const void* q, const void* k, const void* v,
+                       const int32_t* cu_q, const int32_t* cu_k, const int32_t* used_q,
+                       const int32_t* used_k, int32_t nseg, int32_t total_q, int32_t total_k,
+                       int32_t hq, int32_t hkv, int32_t d, int32_t d_v, float softmax_scale,
+                       int32_t causal, void* out, float* lse, void* hip_stream) {
+  int rc = check_sizes(dtype, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
+  if (rc != GVATTN_OK) return rc;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return GVATTN_ERR_INVALID_ARG;
+  if (nseg == 0) return GVATTN_OK;
+  if (!q || !k || !v || !cu_q || !cu_k || !used_q || !used_k || !out || !lse)
+    return GVATTN_ERR_INVALID_ARG;
+  const WsLayout L = noalloc_layout(dtype, nseg, total_q, hq, hkv, d, d_v);
+  if (L.bytes > (size_t)GVATTN_NOALLOC_SCRATCH_BYTES) return GVATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  rc = hip_status(scratch_address(&ws), "scratch address");
+  if (rc != GVATTN_OK) return rc;
+  const Geometry g =
+      make_geom(cu_q, cu_k, used_q, used_k, nseg, total_q, total_k, hq, hkv, d, d_v, causal);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  rc = do_plan(dtype, g, L, ws, s);
+  if (rc != GVATTN_OK) return rc;
+  return do_run(dtype, g, L, q, k, v, softmax_scale, out, lse, ws, s);
 }
 
 int gvattn_lse_merge(int32_t nparts, const void* const* part_out, const float* const* part_lse,

@@ -120,8 +120,11 @@ struct WsLayout {
 // allow_split = false: a plan-only region (the backward's plans), whose work
 // list holds list_splits entries per tile (chunks whose partials live
 // elsewhere).
+// split_bytes caps the split-K partials (a caller with a fixed-size buffer
+// passes what is left of it after the plan).
 inline WsLayout ws_layout(int64_t nseg, int64_t total_q, int hq, int dv, const TileShape& t,
-                          int dtype, bool allow_split = true, int list_splits = 1) {
+                          int dtype, bool allow_split = true, int list_splits = 1,
+                          int64_t split_bytes = kSplitBytes) {
   WsLayout L{};
   L.max_tiles = max_tiles(nseg, total_q, t.rows);
   const int64_t items = L.max_tiles * (hq / t.gf);
@@ -129,7 +132,7 @@ inline WsLayout ws_layout(int64_t nseg, int64_t total_q, int hq, int dv, const T
   if (allow_split && dtype != GVATTN_FP32 && items < kSplitBelow) {
     int64_t s = (kSplitAim + items - 1) / items;
     const int64_t per_split = (int64_t)total_q * hq * (dv + 1) * 4;
-    if (per_split > 0 && s * per_split > kSplitBytes) s = kSplitBytes / per_split;
+    if (per_split > 0 && s * per_split > split_bytes) s = split_bytes / per_split;
     L.splits = (int32_t)(s < 1 ? 1 : (s < kMaxSplits ? s : kMaxSplits));
   }
   size_t b = sizeof(PlanHeader);

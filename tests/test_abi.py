@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     for need in ("gvattn_fwd", "gvattn_lse_merge", "gvattn_fwd_plan", "gvattn_fwd_run",
                  "gvattn_fwd_ranges", "gvattn_bwd", "gvattn_bwd_workspace_size",
                  "gvattn_fwd_workspace_size", "gvattn_status_string",
-                 "gvattn_read_device_error", "gvattn_version"):
+                 "gvattn_read_device_error", "gvattn_version", "gvattn_fwd_noalloc"):
         assert need in names
 
 
@@ -104,6 +104,26 @@ def test_fwd_host_validation(lib, fn):
     assert _fwd(lib, fn, ws_bytes=ok_ws - 1) == B.GVATTN_ERR_WORKSPACE
     # an empty launch is a no-op that needs nothing
     assert _fwd(lib, fn, nseg=0, q=None, ws=None) == B.GVATTN_OK
+
+
+def test_noalloc_host_validation(lib):
+    def call(**over):
+        args = dict(dtype=B.GVATTN_BF16, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE,
+                    used_q=FAKE, used_k=FAKE, nseg=4, total_q=1024, total_k=1024, hq=8, hkv=2,
+                    d=128, dv=128, scale=0.125, causal=0, out=FAKE, lse=FAKE, stream=None)
+        args.update(over)
+        return lib.gvattn_fwd_noalloc(*args.values())
+    assert call(dtype=5) == B.GVATTN_ERR_UNSUPPORTED
+    assert call(d=96) == B.GVATTN_ERR_UNSUPPORTED
+    assert call(hkv=3) == B.GVATTN_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == B.GVATTN_ERR_INVALID_ARG
+    for p in ("q", "k", "v", "cu_q", "cu_k", "used_q", "used_k", "out", "lse"):
+        assert call(**{p: None}) == B.GVATTN_ERR_INVALID_ARG, p
+    # a plan larger than the static scratch is refused before any HIP call
+    assert lib.gvattn_fwd_workspace_size(4, 1 << 30, 1, 1, 64, 64, B.GVATTN_BF16) > \
+        B.GVATTN_NOALLOC_SCRATCH_BYTES
+    assert call(total_q=1 << 30, hq=1, hkv=1, d=64, dv=64) == B.GVATTN_ERR_WORKSPACE
+    assert call(nseg=0, q=None) == B.GVATTN_OK
 
 
 def test_plan_host_validation(lib):
