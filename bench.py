@@ -84,25 +84,58 @@ def algorithmic_bytes(geom, elem=2, keys=None) -> int:
             + uk * geom.hkv * geom.d * elem * 2)
 
 
-def cpu_baseline(wl, flops_fn, seconds: float):
+def cpu_baseline(wl, flops_fn, seconds: float, gpu_out=None, gpu_lse=None):
     """The oracle, as it stands, on the same workload: whole passes over all
-    segments, repeated until about ``seconds`` of CPU work have run."""
+    segments, repeated until about ``seconds`` of CPU work have run.  The
+    first pass's result also gives this run's parity record: the GPU output
+    of the timed steps against the oracle over every used row."""
     import oracle
     g = wl.geom
     workers = oracle.host_cores()
     passes, dt = 0, 0.0
+    ref = None
     while dt < seconds and passes < 20:
         t0 = time.perf_counter()
-        oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k,
-                             float(g.scale), g.causal, workers=workers)
+        r = oracle.attention_fwd(wl.q, wl.k, wl.v, g.cu_q, g.cu_k, g.used_q, g.used_k,
+                                 float(g.scale), g.causal, workers=workers)
         dt += time.perf_counter() - t0
         passes += 1
+        if ref is None:
+            ref = r
     fl = flops_fn(g.used_q, g.used_k) * passes
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
-            "kind": "oracle",
-            "sample": f"{passes} full pass(es) over all {g.nseg} segments and {g.hq} heads of "
-                      f"the same workload, {fl / 1e9:.1f} GFLOP in {dt:.1f} s, FP64 NumPy, "
-                      f"{workers} worker threads"}
+    rec = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
+           "kind": "oracle",
+           "sample": f"{passes} full pass(es) over all {g.nseg} segments and {g.hq} heads of "
+                     f"the same workload, {fl / 1e9:.1f} GFLOP in {dt:.1f} s, FP64 NumPy, "
+                     f"{workers} worker threads"}
+    if gpu_out is not None:
+        rec["parity"] = parity_record(wl, ref, gpu_out, gpu_lse)
+    return rec
+
+
+def parity_record(wl, ref, out, lse) -> dict:
+    """Per-element comparison of the GPU result with the oracle's on every
+    used row: literal max-abs output error, the output-rounding floor
+    max|round(O_ref) - O_ref|, the excess over that floor, the LSE error and
+    the count of elements whose literal error passes 5e-3."""
+    from segmented_varlen_attention_amd import workloads as W
+    g = wl.geom
+    o_ref, l_ref = ref
+    m = np.zeros(g.total_q, bool)
+    for s in range(g.nseg):
+        m[g.cu_q[s]:g.cu_q[s] + g.used_q[s]] = True
+    o_gpu = out.float().cpu().numpy()[m].astype(np.float64)
+    l_gpu = lse.cpu().numpy()[:, m].astype(np.float64)
+    o_ref, l_ref = o_ref[m], l_ref[:, m]
+    err = np.abs(o_gpu - o_ref)
+    floor = np.abs(W.round_to(g.dtype, o_ref.astype(np.float32)).astype(np.float64) - o_ref)
+    fin = np.isfinite(l_ref)
+    return {"rows": int(m.sum()), "max_abs_out_err": float(err.max(initial=0.0)),
+            "rounding_floor": float(floor.max(initial=0.0)),
+            "excess_over_floor": float((err - floor).max(initial=0.0)),
+            "elements_over_5e-3": int(np.count_nonzero(err > 5e-3)),
+            "max_abs_lse_err": float(np.abs(l_gpu[fin] - l_ref[fin]).max(initial=0.0)),
+            "neg_inf_rows_match": bool(np.array_equal(np.isneginf(l_gpu), np.isneginf(l_ref)))}
 
 
 def main():
@@ -115,6 +148,13 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=0.2,
                     help="default warmup length: after the inputs are written the shader "
                          "clock takes about 50 ms of load to settle")
+    ap.add_argument("--settle-seconds", type=float, default=0.25,
+                    help="before the warmup, run the step back to back for this long so "
+                         "that the timed steps see the steady-state clock (reported as "
+                         "'settle'; 0 disables)")
+    ap.add_argument("--evict", action="store_true",
+                    help="also time launches one by one, each after writing a 512 MiB "
+                         "buffer (evicts the 256 MB Infinity Cache)")
     ap.add_argument("--workload", default="causal_replay",
                     choices=["causal_replay", "cfg_cross_attention", "multiview_partitions",
                              "large_head_d256", "ulysses_joint", "decode_batch"])
@@ -236,10 +276,19 @@ def main():
     if wk == "multiview_partitions" and not fused:
         flops = sum(flops_of(g.used_q, u) for _, u in wl.partitions)
 
-    # Warmup.  Right after the input upload and the sentinel fills (or any
-    # idle gap) the first 50-75 steps run up to 35% slower while the clock
-    # settles, so by default the warmup runs for --warmup-seconds; the
-    # count run is what the record reports as "warmup".
+    # Clock settle.  Right after the input upload and the sentinel fills (or
+    # any idle gap) the part's power management holds the shader clock low:
+    # the first 50-75 steps run up to 35% slower.  The settle phase runs the
+    # same step back to back for --settle-seconds before the warmup, so that
+    # the W warmup steps and the K timed steps see the steady-state clock;
+    # the record reports it separately from "warmup".
+    settle_steps, t_s = 0, time.perf_counter()
+    while args.settle_seconds > 0 and time.perf_counter() - t_s < args.settle_seconds:
+        for _ in range(5):
+            step()
+        settle_steps += 5
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_s
     if args.warmup is not None:
         for _ in range(args.warmup):
             step()
@@ -251,46 +300,76 @@ def main():
                 step()
             args.warmup += 5
             torch.cuda.synchronize()
-    log(f"[bench] {args.warmup} warmup steps")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step")
+    log(f"[bench] settle {settle_steps} steps ({settle_s:.2f} s), {args.warmup} warmup steps")
 
-    # main attention kernel alone: the plan stays in the workspace
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    run_only()
-    k0.record(stream)
-    for _ in range(args.steps):
-        run_only()
-    k1.record(stream)
+    def timed(fn, n):
+        """n back-to-back calls with an event on the stream before each one
+        and after the last: (mean, median, min) ms per call."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for i in range(n):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+        return ev[0].elapsed_time(ev[n]) / n, float(np.median(per)), float(per.min())
+
     torch.cuda.synchronize()
-    kern_ms = k0.elapsed_time(k1) / args.steps
+    t_wall = time.perf_counter()
+    ms, med_ms, min_ms = timed(step, args.steps)
+    wall = time.perf_counter() - t_wall
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (events; median {med_ms:.4f}, "
+        f"min {min_ms:.4f}), wall {wall * 1e3 / args.steps:.4f} ms/step")
+
+    # main attention kernel alone: the plan stays in the workspace; the
+    # host-side gap after the timed steps (event readout) is bridged by a
+    # short settle of the same launch
+    t_s = time.perf_counter()
+    while time.perf_counter() - t_s < min(0.1, args.settle_seconds):
+        for _ in range(5):
+            run_only()
+        torch.cuda.synchronize()
+    run_only()
+    kern_ms, kern_med, kern_min = timed(run_only, args.steps)
     kern_flops = (flops_of(g.used_q, launches[0][1].cpu().numpy())
                   if (wk == "multiview_partitions" and not fused) else flops)
-    log(f"[bench] main kernel alone: {kern_ms:.4f} ms/launch")
+    log(f"[bench] main kernel alone: {kern_ms:.4f} ms/launch (median {kern_med:.4f}, "
+        f"min {kern_min:.4f})")
+
+    evict_rec = None
+    if args.evict:
+        # one launch at a time after a 512 MiB write: the step as seen from
+        # a cold Infinity Cache (and after memory-heavy work, which also
+        # lowers the clock for the next tens of ms)
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        per = []
+        for _ in range(args.steps):
+            scratch.fill_(1)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            step()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            per.append(a0.elapsed_time(a1))
+        per = np.array(per)
+        evict_rec = {"launches": args.steps, "mean_ms": round(float(per.mean()), 5),
+                     "median_ms": round(float(np.median(per)), 5),
+                     "min_ms": round(float(per.min()), 5),
+                     "median_TFLOP_per_s": round(flops / (np.median(per) * 1e-3) / 1e12, 3)}
+        log(f"[bench] after 512 MiB eviction: median {evict_rec['median_ms']:.4f} ms")
+        del scratch
 
     merge_rec = None
     if wk == "multiview_partitions" and not fused:
         # the LSE merge alone: algorithmic bytes = both partials, the output
         # and the LSEs, used rows only
-        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         pouts, plses = [p[0] for p in parts], [p[1] for p in parts]
-        m0.record(stream)
-        for _ in range(args.steps):
-            gv.gvattn_lse_merge(pouts, plses, cu_q, used_q, out, lse)
-        m1.record(stream)
-        torch.cuda.synchronize()
-        merge_ms = m0.elapsed_time(m1) / args.steps
+        merge_ms, merge_med, merge_min = timed(
+            lambda: gv.gvattn_lse_merge(pouts, plses, cu_q, used_q, out, lse), args.steps)
         uq = int(np.sum(g.used_q))
         mbytes = uq * g.hq * (len(parts) * (g.dv * 2 + 4) + g.dv * 2 + 4)
-        merge_rec = {"ms": round(merge_ms, 5), "algorithmic_bytes": mbytes,
+        merge_rec = {"ms": round(merge_ms, 5), "median_ms": round(merge_med, 5),
+                     "min_ms": round(merge_min, 5), "algorithmic_bytes": mbytes,
                      "GB_per_s": round(mbytes / (merge_ms * 1e-3) / 1e9, 1),
                      "frac_of_hbm_peak": round(mbytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] LSE merge alone: {merge_ms:.4f} ms, {merge_rec['GB_per_s']} GB/s")
@@ -310,17 +389,13 @@ def main():
         for _ in range(max(1, args.warmup)):
             gv.gvattn_bwd(q, k, v, o0, dout, l0, cu_q, cu_k0, used_q, used_k0, dq, dk, dvv,
                           float(g.scale), g.causal, workspace=bws)
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0.record(stream)
-        for _ in range(args.steps):
-            gv.gvattn_bwd(q, k, v, o0, dout, l0, cu_q, cu_k0, used_q, used_k0, dq, dk, dvv,
-                          float(g.scale), g.causal, workspace=bws)
-        b1.record(stream)
-        torch.cuda.synchronize()
-        bwd_ms = b0.elapsed_time(b1) / args.steps
+        bwd_ms, bwd_med, bwd_min = timed(
+            lambda: gv.gvattn_bwd(q, k, v, o0, dout, l0, cu_q, cu_k0, used_q, used_k0, dq, dk,
+                                  dvv, float(g.scale), g.causal, workspace=bws), args.steps)
         bflops = flops // (2 * g.d + 2 * g.dv) * (6 * g.d + 4 * g.dv)
         btf = bflops / (bwd_ms * 1e-3) / 1e12
-        bwd_rec = {"ms": round(bwd_ms, 5), "flop": bflops, "TFLOP_per_s": round(btf, 3),
+        bwd_rec = {"ms": round(bwd_ms, 5), "median_ms": round(bwd_med, 5),
+                   "min_ms": round(bwd_min, 5), "flop": bflops, "TFLOP_per_s": round(btf, 3),
                    "frac_of_peak": round(btf / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] backward: {bwd_ms:.4f} ms, {btf:.1f} TFLOP/s")
         del dout, dq, dk, dvv, bws
@@ -344,7 +419,10 @@ def main():
     res = {
         "metric": "gapped varlen attn fwd TFLOP/s (used rows) + % of MI355X bf16 MFMA peak",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "median_ms": round(med_ms, 5),
+        "min_ms": round(min_ms, 5),
+        "settle": {"steps": settle_steps, "seconds": round(settle_s, 3)},
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": names[wk].replace("bf16", args.dtype, 1)
                    + ("_fused_keyranges" if fused else ""),
@@ -355,14 +433,19 @@ def main():
                    "algorithmic_hbm_bytes": algorithmic_bytes(
                        g, keys=kr_lens if wl.key_ranges is not None else None)},
         "roofline": roofline,
+        "kernel_alone": {"ms": round(kern_ms, 5), "median_ms": round(kern_med, 5),
+                         "min_ms": round(kern_min, 5)},
     }
+    if evict_rec is not None:
+        res["evict"] = evict_rec
     if merge_rec is not None:
         res["merge"] = merge_rec
     if bwd_rec is not None:
         res["backward"] = bwd_rec
     if not args.no_cpu_baseline and wk == "causal_replay" and args.dtype == "bf16":
         log("[bench] timing the oracle on a bounded sample ...")
-        res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_seconds)
+        # the output buffers hold the last timed launch's result
+        res["cpu_baseline"] = cpu_baseline(wl, flops_of, args.cpu_seconds, out, lse)
     print(json.dumps(res), flush=True)
 
 
