@@ -35,6 +35,8 @@ constexpr int kExactCost = 16;  // a multiple of 2^kGroupShift
 // Segments whose lengths, splits and entry offsets the plan keeps in LDS;
 // a launch with more segments reads them from global memory instead.
 constexpr int kPlanLdsSegs = 2048;
+// Entries the LDS entry -> segment map holds (larger lists search offsets).
+constexpr int kSegMapMax = 24576;
 
 // Exclusive prefix sum over the workgroup: an inclusive scan inside each
 // wave (shuffles), then the wave totals from LDS.  *total gets the sum of
@@ -82,27 +84,35 @@ __device__ int range_error(const PlanArgs& a, int s, int* keys) {
   return 0;
 }
 
-__device__ int segment_error(const PlanArgs& a, int s) {
+// Validates segment s and returns its error bits (0: valid).  *uq and *uk
+// get its used query rows and key count.  The prefix form's six loads are
+// issued together, before any test, so they cost one memory latency.
+__device__ int segment_error(const PlanArgs& a, int s, int* uq_out, int* uk_out) {
   const Geometry& g = a.g;
+  const bool kr = g.kr_off != nullptr;
   const int cq0 = g.cu_q[s], cq1 = g.cu_q[s + 1];
   const int uq = g.used_q[s];
+  const int ck0 = kr ? 0 : g.cu_k[s], ck1 = kr ? 0 : g.cu_k[s + 1];
+  const int uk_p = kr ? 0 : g.used_k[s];
+  *uq_out = uq;
+  *uk_out = 0;
   if (cq0 < 0 || cq1 < cq0 || cq1 > g.total_q) return GVATTN_DEVERR_OFFSETS;
   int err = 0;
   if (uq < 0 || uq > cq1 - cq0) err |= GVATTN_DEVERR_USED_Q;
   // Tiles may run up to 256 rows past a segment's capacity before the
   // bounds-checked loads reject them; keep every such offset below 2^31.
   if ((int64_t)(cq1 - cq0 + 256) * a.q_row_bytes >= (int64_t(1) << 31)) err |= GVATTN_DEVERR_RANGE;
-  if (g.kr_off != nullptr) {
+  if (kr) {
     int keys;
     err |= range_error(a, s, &keys);
     a.ws.seg_keys[s] = err ? 0 : keys;
+    *uk_out = keys;
     return err;
   }
-  const int ck0 = g.cu_k[s], ck1 = g.cu_k[s + 1];
-  const int uk = g.used_k[s];
   if (ck0 < 0 || ck1 < ck0 || ck1 > g.total_k) return err | GVATTN_DEVERR_OFFSETS;
-  if (uk < 0 || uk > ck1 - ck0) err |= GVATTN_DEVERR_USED_K;
+  if (uk_p < 0 || uk_p > ck1 - ck0) err |= GVATTN_DEVERR_USED_K;
   if ((int64_t)(ck1 - ck0 + 256) * a.k_row_bytes >= (int64_t(1) << 31)) err |= GVATTN_DEVERR_RANGE;
+  *uk_out = uk_p;
   return err;
 }
 
@@ -180,6 +190,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int hist[kCostBuckets];
   __shared__ int32_t l_uq[kPlanLdsSegs], l_uk[kPlanLdsSegs], l_split[kPlanLdsSegs];
   __shared__ int32_t l_off[kPlanLdsSegs + 1];
+  __shared__ uint16_t seg_of[kSegMapMax];
   __shared__ int s_err;
   __shared__ int s_max_split;
   __shared__ int s_max_kt;
@@ -191,6 +202,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   v.uk = in_lds ? l_uk : (a.g.kr_off != nullptr ? a.ws.seg_keys : a.g.used_k);
   v.split = in_lds ? l_split : a.ws.seg_split;
   v.off = in_lds ? l_off : a.ws.seg_tile_off;
+  // Without split capacity every segment has one chunk per tile: the entry
+  // offsets are the tile-count prefix sums of step 1 and step 2 is skipped.
+  const bool direct = a.ws.splits == 1;
+  const long long cap = (long long)a.max_tiles * a.ws.splits;
 
   for (int b = tid; b < kCostBuckets; b += kPlanThreads) hist[b] = 0;
   if (tid == 0) {
@@ -201,80 +216,112 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __syncthreads();
 
   // 1. validation and query tiles per segment (an invalid segment: none).
-  //    split holds the segment's tile count until step 2.
+  //    split holds the segment's tile count until step 2 (or 1 when direct;
+  //    the per-segment tables the kernels read go to the workspace as they
+  //    are computed).
   long long n_qtiles = 0;
   for (int base = 0; base < nseg; base += kPlanThreads) {
     const int s = base + tid;
     long long cnt = 0;
     if (s < nseg) {
-      const int err = segment_error(a, s);
-      const int uq = a.g.used_q[s];
-      const int uk = err ? 0 : (a.g.kr_off != nullptr ? a.ws.seg_keys[s] : a.g.used_k[s]);
-      if (err) atomicOr(&s_err, err);
-      else cnt = ((a.mode == 1 ? uk : uq) + a.rows - 1) / a.rows;
-      if (!err && uq > 0) atomicMax(&s_max_kt, (uk + a.key_tile - 1) / a.key_tile);
+      int uq, uk;
+      const int err = segment_error(a, s, &uq, &uk);
+      if (err) {
+        atomicOr(&s_err, err);
+        uk = 0;
+      } else {
+        cnt = ((a.mode == 1 ? uk : uq) + a.rows - 1) / a.rows;
+        if (uq > 0) atomicMax(&s_max_kt, (uk + a.key_tile - 1) / a.key_tile);
+      }
       if (in_lds) {
         l_uq[s] = uq;
         l_uk[s] = uk;
       }
-      v.split[s] = (int32_t)cnt;
+      v.split[s] = direct ? 1 : (int32_t)cnt;
+      if (direct && in_lds) a.ws.seg_split[s] = 1;
     }
     long long tot;
-    block_exclusive_scan<long long>(cnt, wsum64, &tot);
+    const long long excl = block_exclusive_scan<long long>(cnt, wsum64, &tot);
+    if (direct && s < nseg) {
+      const int32_t o = (int32_t)min(n_qtiles + excl, cap);
+      v.off[s] = o;
+      if (in_lds) a.ws.seg_tile_off[s] = o;
+    }
     n_qtiles += tot;
   }
   __threadfence_block();
   __syncthreads();
 
-  // 2. split-K decision, then entry counts and their offsets.  Segments
-  // whose capacities overlap can claim more entries than the list holds;
-  // the whole plan is then rejected (no entries) rather than written past
-  // the workspace.
-  const long long items = n_qtiles * a.n_head_chunks;
-  const bool split_on =
-      a.mode == 0 ? (a.ws.splits > 1 && a.g.kr_off == nullptr && items > 0 && items < kSplitBelow)
-                  : (a.ws.splits > 1 && items > 0 && items < kBwdSplitBelow &&
-                     a.part_slots >= 2 * items);
-  int s_aim = 1;
-  if (split_on && a.mode == 0)
-    s_aim = (int)min((long long)a.ws.splits, (kSplitAim + items - 1) / items);
-  else if (split_on)  // every (entry, KV head) chunk needs a partial slot
-    s_aim = (int)min(min((long long)a.ws.splits, (kBwdSplitAim + items - 1) / items),
-                     (long long)a.part_slots / items);
-  const long long cap = (long long)a.max_tiles * a.ws.splits;
-  long long carry = 0;
-  for (int base = 0; base < nseg; base += kPlanThreads) {
-    const int s = base + tid;
-    long long cnt = 0;
-    if (s < nseg) {
-      const int qt = v.split[s];
-      int S = 1;
-      if (split_on && qt > 0) {
-        if (a.mode == 0) {
-          const int kt = (v.uk[s] + a.key_tile - 1) / a.key_tile;
-          S = max(1, min(s_aim, kt / kMinSplitTiles));
-        } else {  // chunks of at least kBwdMinChunk (head, query tile) steps
-          const int steps = (a.g.hq / a.g.hkv) * ((v.uq[s] + 31) / 32);
-          S = max(1, min(s_aim, steps / kBwdMinChunk));
+  long long carry = n_qtiles;
+  if (!direct) {
+    // 2. split-K decision, then entry counts and their offsets.  Segments
+    // whose capacities overlap can claim more entries than the list holds;
+    // the whole plan is then rejected (no entries) rather than written past
+    // the workspace.
+    const long long items = n_qtiles * a.n_head_chunks;
+    const bool split_on =
+        a.mode == 0 ? (a.g.kr_off == nullptr && items > 0 && items < kSplitBelow)
+                    : (items > 0 && items < kBwdSplitBelow && a.part_slots >= 2 * items);
+    int s_aim = 1;
+    if (split_on && a.mode == 0)
+      s_aim = (int)min((long long)a.ws.splits, (kSplitAim + items - 1) / items);
+    else if (split_on)  // every (entry, KV head) chunk needs a partial slot
+      s_aim = (int)min(min((long long)a.ws.splits, (kBwdSplitAim + items - 1) / items),
+                       (long long)a.part_slots / items);
+    carry = 0;
+    for (int base = 0; base < nseg; base += kPlanThreads) {
+      const int s = base + tid;
+      long long cnt = 0;
+      if (s < nseg) {
+        const int qt = v.split[s];
+        int S = 1;
+        if (split_on && qt > 0) {
+          if (a.mode == 0) {
+            const int kt = (v.uk[s] + a.key_tile - 1) / a.key_tile;
+            S = max(1, min(s_aim, kt / kMinSplitTiles));
+          } else {  // chunks of at least kBwdMinChunk (head, query tile) steps
+            const int steps = (a.g.hq / a.g.hkv) * ((v.uq[s] + 31) / 32);
+            S = max(1, min(s_aim, steps / kBwdMinChunk));
+          }
         }
+        v.split[s] = S;
+        if (in_lds) a.ws.seg_split[s] = S;
+        if (S > 1) atomicMax(&s_max_split, S);
+        cnt = (long long)qt * S;
       }
-      v.split[s] = S;
-      if (S > 1) atomicMax(&s_max_split, S);
-      cnt = (long long)qt * S;
+      long long tot;
+      const long long excl = block_exclusive_scan<long long>(cnt, wsum64, &tot);
+      if (s < nseg) {
+        const int32_t o = (int32_t)min(carry + excl, cap);
+        v.off[s] = o;
+        if (in_lds) a.ws.seg_tile_off[s] = o;
+      }
+      carry += tot;
     }
-    long long tot;
-    const long long excl = block_exclusive_scan<long long>(cnt, wsum64, &tot);
-    if (s < nseg) v.off[s] = (int32_t)min(carry + excl, cap);
-    carry += tot;
   }
   int n_tiles = (int)min(carry, cap);
   if (carry > cap) {
     n_tiles = 0;
     if (tid == 0) s_err |= GVATTN_DEVERR_OFFSETS;
   }
-  if (tid == 0) v.off[nseg] = n_tiles;
+  if (tid == 0) {
+    v.off[nseg] = n_tiles;
+    if (in_lds) a.ws.seg_tile_off[nseg] = n_tiles;
+  }
   __threadfence_block();
   __syncthreads();
+
+  // Entry -> segment map (LDS), so that the two passes over the entries
+  // below look their segment up in one read instead of a binary search.
+  const bool use_map = in_lds && n_tiles <= kSegMapMax;
+  if (use_map) {
+    for (int s = tid; s < nseg; s += kPlanThreads) {
+      const int e1 = v.off[s + 1];
+      for (int e = v.off[s]; e < e1; ++e) seg_of[e] = (uint16_t)s;
+    }
+    __syncthreads();
+  }
+  auto seg_of_entry = [&](int t) { return use_map ? (int)seg_of[t] : find_segment(v.off, nseg, t); };
 
   // 3. histogram of the sort keys.  Forward entries sort by their cost
   // coarsened to 2^kGroupShift key tiles, then by segment, when that key
@@ -295,7 +342,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     return kExactCost + ((cost >> kGroupShift) - (kExactCost >> kGroupShift)) * nseg + (nseg - 1 - s);
   };
   for (int t = tid; t < n_tiles; t += kPlanThreads) {
-    const int s = find_segment(v.off, nseg, t);
+    const int s = seg_of_entry(t);
     int cost;
     make_entry(a, v, s, v.off[s], t, &cost);
     atomicAdd(&hist[sort_key(cost, s)], 1);
@@ -315,20 +362,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // 4. scatter
   for (int t = tid; t < n_tiles; t += kPlanThreads) {
-    const int s = find_segment(v.off, nseg, t);
+    const int s = seg_of_entry(t);
     int cost;
     const int4 e = make_entry(a, v, s, v.off[s], t, &cost);
     const int pos = atomicAdd(&hist[sort_key(cost, s)], 1);
     a.ws.tiles[pos] = e;
-  }
-
-  // the kernels read seg_split (and seg_keys, written in step 1)
-  if (in_lds) {
-    for (int s = tid; s < nseg; s += kPlanThreads) {
-      a.ws.seg_split[s] = l_split[s];
-      a.ws.seg_tile_off[s] = l_off[s];
-    }
-    if (tid == 0) a.ws.seg_tile_off[nseg] = l_off[nseg];
   }
   __syncthreads();
 
