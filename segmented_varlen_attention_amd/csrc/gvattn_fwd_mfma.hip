@@ -568,7 +568,6 @@ void fwd_mfma_kernel(FwdArgs a) {
       __syncthreads();  // the next item's K/V loads reuse the stages
       continue;
     }
-    if (hh == 0 && row < uq) a.lse[(int64_t)head * a.g.total_q + q0 + row] = lse;
     __syncthreads();  // every wave is done with the K/V stages
     T* Os = reinterpret_cast<T*>(lds) + wave * 32 * C::OP;
 #pragma unroll
@@ -580,6 +579,9 @@ void fwd_mfma_kernel(FwdArgs a) {
         for (int cc = 0; cc < 4; ++cc) ov[cc] = (T)(o[db][4 * a4 + cc] * inv);
         *reinterpret_cast<v4*>(Os + r32 * C::OP + db * 32 + 8 * a4 + 4 * hh) = ov;
       }
+    // The LSE store follows the staging writes: the wait that orders those
+    // writes after the last tile's LDS-DMA then does not wait for it.
+    if (hh == 0 && row < uq) a.lse[(int64_t)head * a.g.total_q + q0 + row] = lse;
     __syncthreads();
     {
       T* obase = static_cast<T*>(a.out) + ((int64_t)q0 * a.g.hq + head) * DV;

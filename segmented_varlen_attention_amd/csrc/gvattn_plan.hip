@@ -2,7 +2,7 @@
 // host never reads segment lengths (the PR #302 review objects to host
 // syncs that read them back).
 //
-// One workgroup of 1024 threads:
+// One workgroup of 512 threads:
 //   1. validates every segment and counts its query tiles, ceil(used_q/R);
 //      an invalid segment gets no tiles and sets a device error bit; in the
 //      key-range form it also sums the segment's range lengths (its key
@@ -19,13 +19,20 @@
 // result does not depend on the order, so outputs are deterministic.
 // Segment lengths, splits and offsets stay in LDS for launches of up to
 // kPlanLdsSegs segments (the tile loops then read no global memory), and the
-// prefix sums are wave shuffles plus one exchange of wave totals.
+// prefix sums are wave shuffles plus one exchange of wave totals (up to 64
+// segments or 512 buckets, one wave alone and no exchange).  The kernel is
+// latency-bound: one memory round trip, a few barriers and the LDS
+// atomics.  Each thread takes a contiguous run of entries (one segment
+// lookup for all of them), and the atomics of a wave are aggregated over
+// neighbouring lanes with equal keys.
+#include <type_traits>
+
 #include "gvattn_internal.h"
 
 namespace gvattn {
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 512;
 
 constexpr int kPlanWaves = kPlanThreads / 64;
 // Forward entries are ordered by cost in groups of 2^kGroupShift key tiles,
@@ -35,8 +42,6 @@ constexpr int kExactCost = 16;  // a multiple of 2^kGroupShift
 // Segments whose lengths, splits and entry offsets the plan keeps in LDS;
 // a launch with more segments reads them from global memory instead.
 constexpr int kPlanLdsSegs = 2048;
-// Entries the LDS entry -> segment map holds (larger lists search offsets).
-constexpr int kSegMapMax = 24576;
 
 // Exclusive prefix sum over the workgroup: an inclusive scan inside each
 // wave (shuffles), then the wave totals from LDS.  *total gets the sum of
@@ -64,6 +69,64 @@ __device__ T block_exclusive_scan(T x, T* wsum, T* total) {
   return base + v - x;
 }
 
+// Wave reductions (every lane of the wave takes part).
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+  return x;
+}
+__device__ __forceinline__ int wave_or(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x |= __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Exclusive prefix sum over the 64 lanes of one wave; *total gets the sum.
+template <typename T>
+__device__ __forceinline__ T wave_exclusive_scan(T x, T* total) {
+  const int lane = threadIdx.x & 63;
+  T v = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  *total = __shfl(v, 63, 64);
+  return v - x;
+}
+
+// Wave-aggregated counter update: every lane with `on` takes one slot of
+// cnt[key] and gets its position.  Lanes are grouped into runs of
+// neighbours with equal keys (neighbouring lanes visit neighbouring
+// entries, which mostly share a key); the first lane of a run adds the
+// run's length with one LDS atomic, and lane i of the run takes position
+// old value + i.  Same-address atomics of one instruction are serialised,
+// so this turns up to 64 of them into one.  Every lane of the wave takes
+// part.
+__device__ __forceinline__ int wave_reserve(int* cnt, int key, bool on) {
+  const int lane = threadIdx.x & 63;
+  const int prev_key = __shfl_up(key, 1, 64);
+  const int prev_on = __shfl_up(on ? 1 : 0, 1, 64);
+  const bool head = on && (lane == 0 || prev_on == 0 || prev_key != key);
+  const unsigned long long heads = __ballot(head);
+  const unsigned long long ends = heads | ~__ballot(on);  // a run stops at either
+  const unsigned long long upto = (lane == 63) ? ~0ull : ((1ull << (lane + 1)) - 1ull);
+  const unsigned long long after = ends & ~upto;
+  const int next = after ? __builtin_ctzll(after) : 64;  // first lane past my run
+  int base = 0;
+  if (head) base = atomicAdd(&cnt[key], next - lane);
+  const unsigned long long mine = heads & upto;
+  const int first = (on && mine) ? 63 - __builtin_clzll(mine) : lane;  // my run's head
+  base = __shfl(base, first, 64);
+  return on ? base + (lane - first) : -1;
+}
+
+// x / d for d > 0; d is uniform and almost always a power of two (tile rows,
+// key tile, split count 1), which then costs a shift instead of a division.
+__device__ __forceinline__ int udiv(int x, int d) {
+  return (d & (d - 1)) == 0 ? (int)((unsigned)x >> __builtin_ctz((unsigned)d)) : x / d;
+}
+
 // Key-range form: checks segment s's ranges and returns their total length
 // in *keys (error bits, or 0).
 __device__ int range_error(const PlanArgs& a, int s, int* keys) {
@@ -84,16 +147,33 @@ __device__ int range_error(const PlanArgs& a, int s, int* keys) {
   return 0;
 }
 
-// Validates segment s and returns its error bits (0: valid).  *uq and *uk
-// get its used query rows and key count.  The prefix form's six loads are
-// issued together, before any test, so they cost one memory latency.
-__device__ int segment_error(const PlanArgs& a, int s, int* uq_out, int* uk_out) {
+// The six per-segment values the validation reads (the prefix form; the
+// key-range form reads cu_q and used_q only).
+struct SegLoad {
+  int cq0, cq1, uq, ck0, ck1, uk;
+};
+
+__device__ __forceinline__ SegLoad load_segment(const PlanArgs& a, int s) {
   const Geometry& g = a.g;
   const bool kr = g.kr_off != nullptr;
-  const int cq0 = g.cu_q[s], cq1 = g.cu_q[s + 1];
-  const int uq = g.used_q[s];
-  const int ck0 = kr ? 0 : g.cu_k[s], ck1 = kr ? 0 : g.cu_k[s + 1];
-  const int uk_p = kr ? 0 : g.used_k[s];
+  SegLoad L;
+  L.cq0 = g.cu_q[s];
+  L.cq1 = g.cu_q[s + 1];
+  L.uq = g.used_q[s];
+  L.ck0 = kr ? 0 : g.cu_k[s];
+  L.ck1 = kr ? 0 : g.cu_k[s + 1];
+  L.uk = kr ? 0 : g.used_k[s];
+  return L;
+}
+
+// Validates segment s from its loaded values and returns its error bits (0:
+// valid).  *uq and *uk get its used query rows and key count.
+__device__ int segment_error(const PlanArgs& a, int s, const SegLoad& L, int* uq_out,
+                             int* uk_out) {
+  const Geometry& g = a.g;
+  const bool kr = g.kr_off != nullptr;
+  const int cq0 = L.cq0, cq1 = L.cq1, uq = L.uq;
+  const int ck0 = L.ck0, ck1 = L.ck1, uk_p = L.uk;
   *uq_out = uq;
   *uk_out = 0;
   if (cq0 < 0 || cq1 < cq0 || cq1 > g.total_q) return GVATTN_DEVERR_OFFSETS;
@@ -126,7 +206,7 @@ struct SegView {
 };
 
 // Largest s with off[s] <= t (t < off[nseg]).
-__device__ int find_segment(const int32_t* off, int nseg, int t) {
+__device__ __forceinline__ int find_segment(const int32_t* off, int nseg, int t) {
   int lo = 0, hi = nseg;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -138,7 +218,7 @@ __device__ int find_segment(const int32_t* off, int nseg, int t) {
 
 // Key tiles the query tile at row0 of segment s sees (under bottom-right
 // causal its last row sees the most).
-__device__ int tile_key_tiles(const PlanArgs& a, const SegView& v, int s, int row0) {
+__device__ __forceinline__ int tile_key_tiles(const PlanArgs& a, const SegView& v, int s, int row0) {
   const int uq = v.uq[s];
   const int uk = v.uk[s];
   int kend = uk;
@@ -146,13 +226,14 @@ __device__ int tile_key_tiles(const PlanArgs& a, const SegView& v, int s, int ro
     const int r_last = min(row0 + a.rows, uq) - 1;
     kend = max(0, min(uk, r_last + uk - uq + 1));
   }
-  return (kend + a.key_tile - 1) / a.key_tile;
+  return udiv(kend + a.key_tile - 1, a.key_tile);
 }
 
 // Work entry e (its segment s, first entry of s at e0): query tile
 // (e - e0) / S and key chunk (e - e0) % S of the segment's S = split[s]
 // chunks; the chunk covers key tiles [kt0, kt1) of that query tile.
-__device__ int4 make_entry(const PlanArgs& a, const SegView& v, int s, int e0, int e, int* cost) {
+__device__ __forceinline__ int4 make_entry(const PlanArgs& a, const SegView& v, int s, int e0, int e,
+                                           int* cost) {
   const int S = v.split[s];
   const int local = e - e0;
   if (a.mode == 1) {
@@ -160,24 +241,24 @@ __device__ int4 make_entry(const PlanArgs& a, const SegView& v, int s, int e0, i
     // start at r_first (bottom-right causal); its loop runs over (query
     // head, 32-row query tile), split into S chunks when S > 1 (chunk j of
     // key tile kt is entry e0 + kt * S + j, and e names its partial slot)
-    const int kt = local / S, j = local - kt * S;
+    const int kt = udiv(local, S), j = local - kt * S;
     const int uq = v.uq[s], uk = v.uk[s];
     const int k_row0 = kt * a.rows;
     const int r_first = a.g.causal ? max(0, min(uq, k_row0 + uq - uk)) : 0;
     const int n_it = (a.g.hq / a.g.hkv) * ((uq + 31) / 32 - r_first / 32);
     int it0 = 0, it1 = n_it;
     if (S > 1) {
-      const int chunk = (n_it + S - 1) / S;
+      const int chunk = udiv(n_it + S - 1, S);
       it0 = min(j * chunk, n_it);
       it1 = min(it0 + chunk, n_it);
     }
     *cost = min(it1 - it0, kCostBuckets - 1);
     return make_int4(s, k_row0, r_first, (e << 5) | (j << 1) | (S > 1 ? 1 : 0));
   }
-  const int qt = local / S, j = local - qt * S;
+  const int qt = udiv(local, S), j = local - qt * S;
   const int row0 = qt * a.rows;
   const int nkt = tile_key_tiles(a, v, s, row0);
-  const int chunk = (nkt + S - 1) / S;
+  const int chunk = udiv(nkt + S - 1, S);
   const int kt0 = min(j * chunk, nkt);
   const int kt1 = min(kt0 + chunk, nkt);
   *cost = min(kt1 - kt0, kCostBuckets - 1);
@@ -190,22 +271,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int hist[kCostBuckets];
   __shared__ int32_t l_uq[kPlanLdsSegs], l_uk[kPlanLdsSegs], l_split[kPlanLdsSegs];
   __shared__ int32_t l_off[kPlanLdsSegs + 1];
-  __shared__ uint16_t seg_of[kSegMapMax];
   __shared__ int s_err;
   __shared__ int s_max_split;
   __shared__ int s_max_kt;
+  __shared__ long long s_nq;
   const int tid = threadIdx.x;
   const int nseg = a.g.nseg;
   const bool in_lds = nseg <= kPlanLdsSegs;
-  SegView v;
-  v.uq = in_lds ? l_uq : a.g.used_q;
-  v.uk = in_lds ? l_uk : (a.g.kr_off != nullptr ? a.ws.seg_keys : a.g.used_k);
-  v.split = in_lds ? l_split : a.ws.seg_split;
-  v.off = in_lds ? l_off : a.ws.seg_tile_off;
   // Without split capacity every segment has one chunk per tile: the entry
   // offsets are the tile-count prefix sums of step 1 and step 2 is skipped.
   const bool direct = a.ws.splits == 1;
   const long long cap = (long long)a.max_tiles * a.ws.splits;
+
+  // The first segment of each thread is loaded before the LDS set-up, so
+  // that the set-up and its barrier overlap the memory latency.
+  SegLoad first{};
+  if (tid < nseg) first = load_segment(a, tid);
 
   for (int b = tid; b < kCostBuckets; b += kPlanThreads) hist[b] = 0;
   if (tid == 0) {
@@ -213,44 +294,61 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     s_max_split = 1;
     s_max_kt = 0;
   }
-  __syncthreads();
+  // Up to 64 segments, step 1 runs in wave 0 alone, which wrote the
+  // scalars above itself; the histogram is first used after step 1's
+  // barrier.  More segments: every wave updates the scalars in step 1.
+  const bool one_wave = nseg <= 64;
+  if (!one_wave) __syncthreads();
+
+  // The steps below run with the per-segment tables either all in LDS or
+  // all in the workspace; each form is compiled on its own, so that the LDS
+  // form reads LDS directly (a pointer that may be either would make every
+  // table read wait for all outstanding global stores as well).
+  auto body = [&](const SegView v) __attribute__((always_inline)) {
 
   // 1. validation and query tiles per segment (an invalid segment: none).
-  //    split holds the segment's tile count until step 2 (or 1 when direct;
-  //    the per-segment tables the kernels read go to the workspace as they
-  //    are computed).
+  //    split holds the segment's tile count until step 2 (or 1 when direct).
+  // Up to 64 segments: wave 0 alone, with a wave scan (no block barriers).
   long long n_qtiles = 0;
-  for (int base = 0; base < nseg; base += kPlanThreads) {
+  for (int base = 0; base < nseg && (!one_wave || tid < 64); base += kPlanThreads) {
     const int s = base + tid;
     long long cnt = 0;
+    int err = 0, kt_max = 0;
     if (s < nseg) {
       int uq, uk;
-      const int err = segment_error(a, s, &uq, &uk);
+      err = segment_error(a, s, base == 0 ? first : load_segment(a, s), &uq, &uk);
       if (err) {
-        atomicOr(&s_err, err);
         uk = 0;
       } else {
-        cnt = ((a.mode == 1 ? uk : uq) + a.rows - 1) / a.rows;
-        if (uq > 0) atomicMax(&s_max_kt, (uk + a.key_tile - 1) / a.key_tile);
+        cnt = udiv((a.mode == 1 ? uk : uq) + a.rows - 1, a.rows);
+        if (uq > 0) kt_max = udiv(uk + a.key_tile - 1, a.key_tile);
       }
-      if (in_lds) {
+      if (in_lds) {  // (the workspace form reads the argument arrays)
         l_uq[s] = uq;
         l_uk[s] = uk;
       }
       v.split[s] = direct ? 1 : (int32_t)cnt;
-      if (direct && in_lds) a.ws.seg_split[s] = 1;
+    }
+    // one LDS atomic per wave (the lanes' own atomics would serialise)
+    err = wave_or(err);
+    kt_max = wave_max(kt_max);
+    if ((tid & 63) == 0) {
+      if (err) atomicOr(&s_err, err);
+      if (kt_max > 0) atomicMax(&s_max_kt, kt_max);
     }
     long long tot;
-    const long long excl = block_exclusive_scan<long long>(cnt, wsum64, &tot);
+    const long long excl = one_wave ? wave_exclusive_scan<long long>(cnt, &tot)
+                                    : block_exclusive_scan<long long>(cnt, wsum64, &tot);
     if (direct && s < nseg) {
       const int32_t o = (int32_t)min(n_qtiles + excl, cap);
       v.off[s] = o;
-      if (in_lds) a.ws.seg_tile_off[s] = o;
     }
     n_qtiles += tot;
   }
+  if (one_wave && tid == 0) s_nq = n_qtiles;
   __threadfence_block();
   __syncthreads();
+  if (one_wave) n_qtiles = s_nq;
 
   long long carry = n_qtiles;
   if (!direct) {
@@ -272,12 +370,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     for (int base = 0; base < nseg; base += kPlanThreads) {
       const int s = base + tid;
       long long cnt = 0;
+      int s_wave = 1;
       if (s < nseg) {
         const int qt = v.split[s];
         int S = 1;
         if (split_on && qt > 0) {
           if (a.mode == 0) {
-            const int kt = (v.uk[s] + a.key_tile - 1) / a.key_tile;
+            const int kt = udiv(v.uk[s] + a.key_tile - 1, a.key_tile);
             S = max(1, min(s_aim, kt / kMinSplitTiles));
           } else {  // chunks of at least kBwdMinChunk (head, query tile) steps
             const int steps = (a.g.hq / a.g.hkv) * ((v.uq[s] + 31) / 32);
@@ -285,16 +384,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
           }
         }
         v.split[s] = S;
-        if (in_lds) a.ws.seg_split[s] = S;
-        if (S > 1) atomicMax(&s_max_split, S);
         cnt = (long long)qt * S;
+        s_wave = S;
       }
+      s_wave = wave_max(s_wave);
+      if ((tid & 63) == 0 && s_wave > 1) atomicMax(&s_max_split, s_wave);
       long long tot;
       const long long excl = block_exclusive_scan<long long>(cnt, wsum64, &tot);
       if (s < nseg) {
         const int32_t o = (int32_t)min(carry + excl, cap);
         v.off[s] = o;
-        if (in_lds) a.ws.seg_tile_off[s] = o;
       }
       carry += tot;
     }
@@ -304,24 +403,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     n_tiles = 0;
     if (tid == 0) s_err |= GVATTN_DEVERR_OFFSETS;
   }
-  if (tid == 0) {
-    v.off[nseg] = n_tiles;
-    if (in_lds) a.ws.seg_tile_off[nseg] = n_tiles;
-  }
+  if (tid == 0) v.off[nseg] = n_tiles;
   __threadfence_block();
   __syncthreads();
-
-  // Entry -> segment map (LDS), so that the two passes over the entries
-  // below look their segment up in one read instead of a binary search.
-  const bool use_map = in_lds && n_tiles <= kSegMapMax;
-  if (use_map) {
-    for (int s = tid; s < nseg; s += kPlanThreads) {
-      const int e1 = v.off[s + 1];
-      for (int e = v.off[s]; e < e1; ++e) seg_of[e] = (uint16_t)s;
-    }
-    __syncthreads();
-  }
-  auto seg_of_entry = [&](int t) { return use_map ? (int)seg_of[t] : find_segment(v.off, nseg, t); };
 
   // 3. histogram of the sort keys.  Forward entries sort by their cost
   // coarsened to 2^kGroupShift key tiles, then by segment, when that key
@@ -341,34 +425,118 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (!grouped || cost < kExactCost) return cost;
     return kExactCost + ((cost >> kGroupShift) - (kExactCost >> kGroupShift)) * nseg + (nseg - 1 - s);
   };
-  for (int t = tid; t < n_tiles; t += kPlanThreads) {
-    const int s = seg_of_entry(t);
-    int cost;
-    make_entry(a, v, s, v.off[s], t, &cost);
-    atomicAdd(&hist[sort_key(cost, s)], 1);
+  // Each thread takes a contiguous run of entries, so that one segment
+  // lookup serves all of them.
+  const int per = (n_tiles + kPlanThreads - 1) / kPlanThreads;
+  const int e_begin = min(tid * per, n_tiles);
+  const int e_end = min(e_begin + per, n_tiles);
+  // Step i of the walk visits entry e_begin + i of every thread (the same
+  // trip count in every lane, so that the counter updates of a step can be
+  // aggregated over the wave).  steps_c: a compile-time step count (the
+  // loop unrolls and step i is a constant), or 0 for `per` steps.
+  auto walk = [&](auto steps_c, auto&& visit) {
+    constexpr int N = decltype(steps_c)::value;
+    int s = 0, e0 = 0, e1 = 0;
+    if (e_begin < e_end) {
+      s = find_segment(v.off, nseg, e_begin);
+      e0 = v.off[s];
+      e1 = v.off[s + 1];
+    }
+    const int n = N > 0 ? N : per;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const int t = e_begin + i;
+      const bool on = i < per && t < e_end;
+      int4 e = make_int4(0, 0, 0, 0);
+      int key = 0;
+      if (on) {
+        while (t >= e1) {  // segments without entries are passed over
+          ++s;
+          e0 = e1;
+          e1 = v.off[s + 1];
+        }
+        int cost;
+        e = make_entry(a, v, s, e0, t, &cost);
+        key = sort_key(cost, s);
+      }
+      visit(i, e, key, on);
+    }
+  };
+  // Up to four entries per thread, the scatter reuses the entries, keys and
+  // in-bucket ranks of the histogram pass from registers.
+  constexpr int kCached = 4;
+  const bool cached = per <= kCached;
+  int4 c_ent[kCached];
+  int c_key[kCached], c_rank[kCached];
+  bool c_on[kCached];
+  if (cached) {
+    walk(std::integral_constant<int, kCached>{}, [&](int i, const int4& e, int key, bool on) {
+      c_ent[i] = e;
+      c_key[i] = key;
+      c_on[i] = on;
+      c_rank[i] = wave_reserve(hist, key, on);
+    });
+  } else {
+    walk(std::integral_constant<int, 0>{},
+         [&](int, const int4&, int key, bool on) { wave_reserve(hist, key, on); });
   }
   __syncthreads();
 
-  // bucket start positions, most expensive bucket first
-  static_assert(kCostBuckets == 2 * kPlanThreads, "two buckets per thread");
-  const int b_hi = kCostBuckets - 1 - 2 * tid;  // visited first
-  const int b_lo = b_hi - 1;
-  const int c_hi = hist[b_hi], c_lo = hist[b_lo];
-  int tot;
-  const int excl = block_exclusive_scan<int>(c_hi + c_lo, wsum, &tot);
-  hist[b_hi] = excl;
-  hist[b_lo] = excl + c_hi;
-  __syncthreads();
-
-  // 4. scatter
-  for (int t = tid; t < n_tiles; t += kPlanThreads) {
-    const int s = seg_of_entry(t);
-    int cost;
-    const int4 e = make_entry(a, v, s, v.off[s], t, &cost);
-    const int pos = atomicAdd(&hist[sort_key(cost, s)], 1);
-    a.ws.tiles[pos] = e;
+  // bucket start positions, most expensive bucket first.  Forward keys
+  // stay below n_keys; up to 512 buckets, wave 0 scans them alone (eight
+  // per lane), else every thread takes two.
+  const int n_keys =
+      a.mode != 0 ? kCostBuckets
+                  : (grouped ? kExactCost + ((max_kt >> kGroupShift) - (kExactCost >> kGroupShift) + 1) * nseg
+                             : max_kt + 1);
+  if (n_keys <= 512) {
+    if (tid < 64) {
+      int c[8], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int b = n_keys - 1 - (8 * tid + j);
+        c[j] = b >= 0 ? hist[b] : 0;
+        sum += c[j];
+      }
+      int tot;
+      int run = wave_exclusive_scan<int>(sum, &tot);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int b = n_keys - 1 - (8 * tid + j);
+        if (b >= 0) hist[b] = run;
+        run += c[j];
+      }
+    }
+  } else {
+    constexpr int kPer = kCostBuckets / kPlanThreads;  // buckets per thread
+    static_assert(kCostBuckets == kPer * kPlanThreads, "buckets split evenly");
+    int c[kPer], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      c[j] = hist[kCostBuckets - 1 - (kPer * tid + j)];  // visited first: the highest
+      sum += c[j];
+    }
+    int tot;
+    int run = block_exclusive_scan<int>(sum, wsum, &tot);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      hist[kCostBuckets - 1 - (kPer * tid + j)] = run;
+      run += c[j];
+    }
   }
   __syncthreads();
+
+  // 4. scatter (the header below takes nothing from it: no barrier)
+  if (cached) {  // hist holds the bucket starts now
+#pragma unroll
+    for (int i = 0; i < kCached; ++i)
+      if (c_on[i]) a.ws.tiles[hist[c_key[i]] + c_rank[i]] = c_ent[i];
+  } else {
+    walk(std::integral_constant<int, 0>{}, [&](int, const int4& e, int key, bool on) {
+      const int pos = wave_reserve(hist, key, on);
+      if (on) a.ws.tiles[pos] = e;
+    });
+  }
 
   if (tid == 0) {
     a.ws.header->n_tiles = n_tiles;
@@ -376,6 +544,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.ws.header->key = a.key;
     a.ws.header->rows_per_tile = a.rows;
     a.ws.header->max_split = s_max_split;
+  }
+  // The LDS form's tables go to the workspace last (they are final since
+  // step 2), with no barrier after them.
+  if (in_lds) {
+    for (int i = tid; i < nseg; i += kPlanThreads) {
+      a.ws.seg_split[i] = v.split[i];
+      a.ws.seg_tile_off[i] = v.off[i];
+    }
+    if (tid == 0) a.ws.seg_tile_off[nseg] = v.off[nseg];
+  }
+  };
+  if (in_lds) {
+    body(SegView{l_uq, l_uk, l_split, l_off});
+  } else {
+    body(SegView{a.g.used_q, a.g.kr_off != nullptr ? a.ws.seg_keys : a.g.used_k, a.ws.seg_split,
+                 a.ws.seg_tile_off});
   }
 }
 
