@@ -410,6 +410,7 @@ def main():
         gbs = algorithmic_bytes(g) / (kern_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    alg_bytes = algorithmic_bytes(g, keys=kr_lens if wl.key_ranges is not None else None)
     names = {"cfg_cross_attention": "bf16_cfg_cross_attn_b2_4096q_text24_700_gqa32x8_d128",
              "causal_replay": "bf16_causal_gapped_replay_64x2048_gqa32x8_d128",
              "multiview_partitions": "bf16_multiview_8x8190q_32760k_2partitions_merge_gqa24x8_d128",
@@ -430,11 +431,15 @@ def main():
                    "used_q_rows": int(np.sum(g.used_q)), "hq": g.hq, "hkv": g.hkv, "d": g.d,
                    "causal": bool(g.causal), "flop_per_step": flops,
                    "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-                   "algorithmic_hbm_bytes": algorithmic_bytes(
-                       g, keys=kr_lens if wl.key_ranges is not None else None)},
+                   "algorithmic_hbm_bytes": alg_bytes},
         "roofline": roofline,
         "kernel_alone": {"ms": round(kern_ms, 5), "median_ms": round(kern_med, 5),
-                         "min_ms": round(kern_min, 5)},
+                         "min_ms": round(kern_min, 5),
+                         # the same launch against the HBM roofline: used inputs and
+                         # outputs, each once, over the mean launch time
+                         "hbm_GB_per_s": round(alg_bytes / (kern_ms * 1e-3) / 1e9, 1),
+                         "frac_of_hbm_peak": round(alg_bytes / (kern_ms * 1e-3) / 1e9
+                                                   / PEAK_HBM_GBS, 4)},
     }
     if evict_rec is not None:
         res["evict"] = evict_rec
