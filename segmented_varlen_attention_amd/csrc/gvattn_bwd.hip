@@ -332,7 +332,7 @@ __global__ __launch_bounds__(64 * GF * RB, 2) void bwd_dq_kernel(BwdArgs a) {
         const int idx = it * 64 + lane;
         const int rr = idx / C::CHK, ch = idx % C::CHK;
         const u32x4 val = *reinterpret_cast<const u32x4*>(Ss + rr * C::KP + 8 * ch);
-        buf_store16(dqr, (uint32_t)(wr0 + rr) * qstride + ch * 16, val);
+        buf_store16_nt(dqr, (uint32_t)(wr0 + rr) * qstride + ch * 16, val);
       }
     }
     __syncthreads();
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
         const int rr = idx / ch_row, ch = idx % ch_row;
         if (rr < 32) {
           const u32x4 val = *reinterpret_cast<const u32x4*>(Ws + rr * PMAX + 8 * ch);
-          buf_store16(orr, (uint32_t)(wk0 + rr) * stride + ch * 16, val);
+          buf_store16_nt(orr, (uint32_t)(wk0 + rr) * stride + ch * 16, val);
         }
       }
     }

@@ -34,6 +34,8 @@
 //     its weight is not exactly 1).
 //   * Rows that see at most one tile of keys add the rounding remainder of
 //     P as a second product on that tile.
+//   * O rows leave through LDS staging as full-row stores with the
+//     non-temporal policy (nothing reads them again; K/V keeps the L2).
 //   * Buffer resources end at the segment's last used row: loads past it
 //     return zero (ragged key tiles, gap rows, buffer ends) and stores past
 //     it are dropped (gap rows of O stay bit-exact).  Key-padding and causal
@@ -591,7 +593,7 @@ void fwd_mfma_kernel(FwdArgs a) {
         const int idx = it * 64 + lane;
         const int r = idx / C::CHV, ch = idx % C::CHV;
         const u32x4 val = *reinterpret_cast<const u32x4*>(Os + r * C::OP + 8 * ch);
-        buf_store16(orr, (uint32_t)(wr0 + r) * ostride + ch * 16, val);
+        buf_store16_nt(orr, (uint32_t)(wr0 + r) * ostride + ch * 16, val);
       }
     }
     __syncthreads();  // staging area is reused by the next item's K/V loads

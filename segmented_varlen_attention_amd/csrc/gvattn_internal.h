@@ -375,6 +375,13 @@ __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
 
+// The same with the non-temporal policy (gfx950 cache-policy bit `nt`), for
+// output nothing in the kernel reads again: its lines then leave the L2
+// early instead of displacing K/V that later tiles still read.
+__device__ inline void buf_store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 2);
+}
+
 __device__ inline float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }

@@ -33,7 +33,9 @@ constexpr int kElems = 32;  // split merge: elements of one (row, head) per lane
 constexpr int kMergeElems = 16;
 
 // 8 elements of type T: 16-byte loads into raw registers, unpacking to
-// FP32, and packing / storing FP32 back as T (round to nearest even).
+// FP32, and packing / storing FP32 back as T (round to nearest even).  The
+// stores are non-temporal: nothing here reads the output again, and
+// streaming it past the L2 leaves more of it for the partials' reads.
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> {
   static constexpr int kRaw = 1;  // 16-byte registers per 8 elements
@@ -48,7 +50,7 @@ template <> struct Vec8<__bf16> {
     bf16x8 o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = (__bf16)f[i];
-    *reinterpret_cast<bf16x8*>(p) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<bf16x8*>(p));
   }
 };
 template <> struct Vec8<_Float16> {
@@ -63,7 +65,7 @@ template <> struct Vec8<_Float16> {
     f16x8 o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = (_Float16)f[i];
-    *reinterpret_cast<f16x8*>(p) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(p));
   }
 };
 template <> struct Vec8<float> {
@@ -86,8 +88,8 @@ template <> struct Vec8<float> {
       a[i] = f[i];
       b[i] = f[4 + i];
     }
-    reinterpret_cast<f32x4*>(p)[0] = a;
-    reinterpret_cast<f32x4*>(p)[1] = b;
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p) + 1);
   }
 };
 
