@@ -458,11 +458,20 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
       const auto ors = make_rsrc(static_cast<const T*>(a.dout) + ((int64_t)q0 * a.g.hq + head) * DV, obytes);
       const auto srs = make_rsrc(a.stats + ((int64_t)head * a.g.total_q + q0) * 2, (uint32_t)uq * 8u);
       const uint32_t oq = (uint32_t)ld_qt * 32 * qstride, oo = (uint32_t)ld_qt * 32 * ostride;
+      // The row statistics first, with the lane index recomputed here (not
+      // kept, where it was spilled): a wait for a spill reload after the tile
+      // loads would also wait for those loads, one memory latency per step
+      // for wave 0 and, through the barriers, for the workgroup.
+      if (wave == 0) {
+        // In asm so that it is not merged with the spilled copy of the index.
+        uint32_t l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        dma4(srs, st + Q_TILE + O_TILE, (uint32_t)ld_qt * 256u + l * 4u);
+      }
 #pragma unroll
       for (int i = 0; i < NDMA_Q; ++i) dma16(qrs, st + (wave + i * NW) * 1024, qoff[i] + oq, 0);
 #pragma unroll
       for (int i = 0; i < NDMA_O; ++i) dma16(ors, st + Q_TILE + (wave + i * NW) * 1024, ooff[i] + oo, 0);
-      if (wave == 0) dma4(srs, st + Q_TILE + O_TILE, (uint32_t)ld_qt * 256u + lane * 4u);
       if (++ld_qt == qt_end) {
         ld_qt = qt_first;
         ++ld_h;
