@@ -98,25 +98,39 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds_dst, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, voff, 0, 0, 0);
 }
 
+// XOR swizzle of the 16-byte chunk index of a tile row (W 16-bit elements
+// per row) for tiles read both ways: as rows (16 bytes per lane, 16
+// consecutive rows at one logical chunk per clock) and transposed
+// (ds_read_b64_tr_b16: 4 consecutive rows x 4 chunks per 32 lanes).  Rows
+// need 16 distinct slots of the 256-byte bank window across 16 consecutive
+// rows; transposed reads need the four rows of an aligned group of four in
+// distinct 64-byte quarters of it.  At W = 128 the swizzle is a bijection
+// of (row mod 16) whose bits 2-3 come from row bits 0-1; at W = 64 (two
+// rows per window) the same holds for each row parity.
+template <int W>
+__device__ __forceinline__ int swz_kt(int row) {
+  return (W == 64) ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : (((row & 3) << 2) | ((row >> 2) & 3));
+}
+
 // 32 x 32 block of the A operand transposed: lane (r32, hh) receives
 // column `col0 + r32` of rows {16 * a2 + 8 * (j / 4) + 4 * hh + j % 4}, j < 8,
-// of a row-major tile with `pitch` bytes per row and swizzle swz_k<W>.
+// of a row-major tile with W 16-bit elements per row and swizzle swz_kt<W>.
 template <int W, typename v8>
 __device__ __forceinline__ v8 read_a_transposed(const char* tile, int a2, int col0, int trow,
                                                 int tcol) {
   const int dcol = col0 + tcol;
   const int ch = dcol >> 3, within = (dcol & 7) * 2;
   const int r_lo = a2 * 16 + trow, r_hi = r_lo + 8;
-  const i16x4 lo = read_tr(tile + r_lo * (W * 2) + ((ch ^ swz_k<W>(r_lo)) << 4) + within);
-  const i16x4 hi = read_tr(tile + r_hi * (W * 2) + ((ch ^ swz_k<W>(r_hi)) << 4) + within);
+  const i16x4 lo = read_tr(tile + r_lo * (W * 2) + ((ch ^ swz_kt<W>(r_lo)) << 4) + within);
+  const i16x4 hi = read_tr(tile + r_hi * (W * 2) + ((ch ^ swz_kt<W>(r_hi)) << 4) + within);
   return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Row r32, k-step kk of a row-major tile with W elements per row, swizzle
-// swz_k<W>: the A operand of a product whose k index runs over the row.
+// swz_kt<W>: the A operand of a product whose k index runs over the row.
 template <int W, typename v8>
 __device__ __forceinline__ v8 read_a_rows(const char* tile, int r32, int hh, int kk) {
-  return *reinterpret_cast<const v8*>(tile + r32 * (W * 2) + (((2 * kk + hh) ^ swz_k<W>(r32)) << 4));
+  return *reinterpret_cast<const v8*>(tile + r32 * (W * 2) + (((2 * kk + hh) ^ swz_kt<W>(r32)) << 4));
 }
 
 // ---------------------------------------------------------------------------
@@ -163,13 +177,13 @@ __global__ __launch_bounds__(64 * GF * RB, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int i = 0; i < NDMA_K; ++i) {
     const int s = (wave + i * NW) * 64 + lane;
     const int row = s / C::CHK, pc = s % C::CHK;
-    koff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_k<D>(row)) * 16);
+    koff[i] = (uint32_t)row * kstride + (uint32_t)((pc ^ swz_kt<D>(row)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < NDMA_V; ++i) {
     const int s = (wave + i * NW) * 64 + lane;
     const int row = s / C::CHV, pc = s % C::CHV;
-    voff[i] = (uint32_t)row * vstride + (uint32_t)((pc ^ swz_k<DV>(row)) * 16);
+    voff[i] = (uint32_t)row * vstride + (uint32_t)((pc ^ swz_kt<DV>(row)) * 16);
   }
   // transposed-read addressing (see read_a_transposed)
   const int il = lane & 15;
@@ -389,20 +403,22 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
   const uint32_t vstride = (uint32_t)hkv * DV * 2;
   const uint32_t ostride = (uint32_t)a.g.hq * DV * 2;
   const float c = a.scale_log2;
-  float* Px = reinterpret_cast<float*>(lds + P_OFF + pair * P_BYTES) + lane * 16;
+  // P of the pair: float4 i of lane l at (i * 64 + l) * 16 bytes, so that
+  // the 64 lanes of one access fill consecutive 16-byte slots
+  float* Px = reinterpret_cast<float*>(lds + P_OFF + pair * P_BYTES) + lane * 4;
 
   uint32_t qoff[NDMA_Q], ooff[NDMA_O];
 #pragma unroll
   for (int i = 0; i < NDMA_Q; ++i) {
     const int s = (wave + i * NW) * 64 + lane;
     const int row = s / C::CHK, pc = s % C::CHK;
-    qoff[i] = (uint32_t)row * qstride + (uint32_t)((pc ^ swz_k<D>(row)) * 16);
+    qoff[i] = (uint32_t)row * qstride + (uint32_t)((pc ^ swz_kt<D>(row)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < NDMA_O; ++i) {
     const int s = (wave + i * NW) * 64 + lane;
     const int row = s / C::CHV, pc = s % C::CHV;
-    ooff[i] = (uint32_t)row * ostride + (uint32_t)((pc ^ swz_k<DV>(row)) * 16);
+    ooff[i] = (uint32_t)row * ostride + (uint32_t)((pc ^ swz_kt<DV>(row)) * 16);
   }
   const int il = lane & 15;
   const int trow = 4 * hh + (il >> 2);
@@ -550,7 +566,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
               f32x4 x;
   #pragma unroll
               for (int j = 0; j < 4; ++j) x[j] = s[4 * i + j];
-              *reinterpret_cast<f32x4*>(Px + 4 * i) = x;
+              *reinterpret_cast<f32x4*>(Px + 256 * i) = x;
             }
   #pragma unroll
             for (int v = 0; v < 16; ++v) opb[v >> 3][v & 7] = (T)s[v];
@@ -570,7 +586,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
             __syncthreads();  // P of this tile is in LDS
   #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const f32x4 x = *reinterpret_cast<const f32x4*>(Px + 4 * i);
+              const f32x4 x = *reinterpret_cast<const f32x4*>(Px + 256 * i);
   #pragma unroll
               for (int j = 0; j < 4; ++j) dp[4 * i + j] *= x[j];
             }
