@@ -41,6 +41,17 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source additions.  The forward's d > 128 kernels run one wave per SIMD
+# with up to 512 registers; by default their MFMAs would accumulate in AGPRs
+# and every vector operation on O or the scores would copy them to VGPRs and
+# back.  The VGPR form keeps O and the scores in VGPRs (the Q fragments,
+# only ever a matrix-core operand, are placed in AGPRs by the kernel).
+# Kernels with at most 256 registers per wave use the VGPR form anyway.
+SOURCE_FLAGS = {
+    "gvattn_fwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -67,7 +78,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     jobs = jobs or min(len(cmds), 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

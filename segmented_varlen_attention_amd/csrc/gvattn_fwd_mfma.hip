@@ -536,9 +536,242 @@ void fwd_mfma_kernel(FwdArgs a) {
         tile_step(kt, std::integral_constant<int, 0>{});
         if (kt + 1 < kt_end) tile_step(kt + 1, std::integral_constant<int, 1>{});
       }
+    } else if constexpr (!KR) {
+      // One workgroup per CU (d > 128), so one wave per SIMD: no other wave
+      // fills the matrix cores while this one runs its softmax.  The loop is
+      // software-pipelined instead, with K one tile ahead of V.  Step t takes
+      // the row max of tile t (and the rare rescale), then computes the
+      // scores of tile t + 1 in one straight-line block with the
+      // exponentials and 16-bit conversion of tile t, so that matrix-core
+      // and vector instructions interleave, then P.V of tile t.  K(t) and
+      // V(t) sit in stage (t - kt_begin) & 1 as in the loop above; step t
+      // loads K(t + 2) into the stage K(t) leaves and V(t + 1) into the one
+      // V(t - 1) left.  Past the last tile the loads go through zero-size
+      // resources (zeros into stages nobody reads), so the scores of the
+      // tile after the last one are computed, from zeros, and dropped.
+      auto stage_of = [&](int kt) __attribute__((always_inline)) {
+        return lds + ((kt - kt_begin) & 1) * C::STAGE_BYTES;
+      };
+      auto score_mfma = [&](const char* Ks, f32x16 (&sv)[C::NKB_], int kk, int kb)
+                            __attribute__((always_inline)) {
+        const int krow = kb * 32 + r32;
+        const v8 ka = *reinterpret_cast<const v8*>(Ks + krow * (DQ * 2) +
+                                                   (((2 * kk + hh) ^ swz_k<DQ>(krow)) << 4));
+        sv[kb] = E::mfma(ka, qf[kk], sv[kb]);
+      };
+      // P.V with the V^T operands read PD products ahead (one wave per SIMD:
+      // no other wave hides the LDS latency), consecutive products
+      // accumulating into different O blocks
+      constexpr int PD = 3;
+      auto pv_tile = [&](const char* Vs, const v8 (&p)[C::NKB_][2], auto&& work)
+                         __attribute__((always_inline)) {
+        auto v_operand = [&](int idx) __attribute__((always_inline)) {
+          const int db = idx % C::DB, ka = idx / C::DB;
+          const int dcol = db * 32 + vd_l;
+          const int ch = dcol >> 3, within = (dcol & 7) * 2;
+          const int r_lo = (ka >> 1) * 32 + (ka & 1) * 16 + vrow_l;
+          const int r_hi = r_lo + 8;
+          const i16x4 lo = read_tr(Vs + r_lo * (DV * 2) + ((ch ^ swz_v<DV>(r_lo)) << 4) + within);
+          const i16x4 hi = read_tr(Vs + r_hi * (DV * 2) + ((ch ^ swz_v<DV>(r_hi)) << 4) + within);
+          return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        constexpr int NPV = C::DB * C::NKB_ * 2;
+        v8 ring[PD];
+#pragma unroll
+        for (int i = 0; i < PD - 1; ++i) ring[i] = v_operand(i);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+          if (i + PD - 1 < NPV) ring[(i + PD - 1) % PD] = v_operand(i + PD - 1);
+          asm volatile("" ::: "memory");  // the reads stay here, ahead of their use
+          const int db = i % C::DB, ka = i / C::DB;
+          o[db] = E::mfma(ring[i % PD], p[ka >> 1][ka & 1], o[db]);
+          work(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // key-padding / causal mask of a score tile starting at key kbase
+      auto mask_tile = [&](f32x16 (&sv)[C::NKB_], int kbase) __attribute__((always_inline)) {
+        if (kbase + C::BN > lim_w) {
+          int nv = lim - kbase - 4 * hh;
+          asm volatile("" : "+v"(nv));
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (kb * 32 + 8 * (v >> 2) + (v & 3) >= nv) sv[kb][v] = -INFINITY;
+        }
+      };
+      // Row max of a score tile (lane max mx, both halves) against the
+      // running max: raise it and rescale O when it grew by more than 2^8.
+      // Returns the max the weights of that tile are taken against.
+      auto settle_max = [&](float mx, bool valid) __attribute__((always_inline)) {
+        mx = fmaxf(mx, max_across_halves(mx));
+        const float cand = valid ? mx * c : -INFINITY;
+        if (__any(cand > m_run + 8.f)) {
+          keep_branch();
+          const float m_new = fmaxf(m_run, cand);
+          const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+          lh_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
+        }
+        return (m_run == -INFINITY) ? 0.f : m_run;
+      };
+
+      f32x16 sc[C::NKB_];
+#pragma unroll
+      for (int kb = 0; kb < C::NKB_; ++kb) sc[kb] = f32x16{};
+      if (kt_begin < kt_end) {
+        wait_vmem();
+        __syncthreads();
+        // K of the second tile into stage 1, then the scores of the first
+        const int kn = kt_begin + 1;
+        const auto krn = k_rsrc(k0, kn < kt_end ? uk : 0);
+        char* st = lds + C::STAGE_BYTES;
+        const uint32_t soff = (uint32_t)kn * C::BN * kstride;
+#pragma unroll
+        for (int i = 0; i < C::NDMA_K; ++i) {
+          const int inst = wave + i * C::NW;
+          if (C::DMA_K % C::NW == 0 || i + 1 < C::NDMA_K || inst < C::DMA_K)
+            dma16(krn, st + inst * 1024, koff[i], soff);
+        }
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb) score_mfma(lds, sc, kk, kb);
+      }
+      float m_use = 0.f;
+      if (kt_begin < kt_end) {
+        mask_tile(sc, kt_begin * C::BN);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
+        m_use = settle_max(mx, true);
+      }
+      for (int kt = kt_begin; kt < kt_end; ++kt) {
+        // Q is only a matrix-core operand: keep it in AGPRs, which leaves
+        // the VGPRs to O and the two score tiles
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) asm volatile("" : "+a"(qf[kk]));
+        wait_vmem();
+        __syncthreads();  // K(kt + 1) and V(kt) are in; K(kt), V(kt - 1) are free
+        const char* Vs = stage_of(kt) + C::K_TILE_BYTES;
+        const char* Kn = stage_of(kt + 1);
+        const auto krn = k_rsrc(k0, kt + 2 < kt_end ? uk : 0);
+        const auto vrn = v_rsrc(k0, kt + 1 < kt_end ? uk : 0);
+        char* stk = stage_of(kt);
+        char* stv = stage_of(kt + 1) + C::K_TILE_BYTES;
+        const uint32_t soffk = (uint32_t)(kt + 2) * C::BN * kstride;
+        const uint32_t soffv = (uint32_t)(kt + 1) * C::BN * vstride;
+        // (the range test is a branch only when the waves do not share the
+        // instructions evenly)
+        auto issue_one = [&](int j) __attribute__((always_inline)) {
+          if (j < C::NDMA_K) {
+            const int inst = wave + j * C::NW;
+            if (C::DMA_K % C::NW == 0 || j + 1 < C::NDMA_K || inst < C::DMA_K)
+              dma16(krn, stk + inst * 1024, koff[j], soffk);
+          } else {
+            const int i = j - C::NDMA_K;
+            const int inst = wave + i * C::NW;
+            if (C::DMA_V % C::NW == 0 || i + 1 < C::NDMA_V || inst < C::DMA_V)
+              dma16(vrn, stv + inst * 1024, voff[i], soffv);
+          }
+        };
+
+        const int kbase = kt * C::BN;
+
+        // Scores of tile kt + 1 (and the loads of step kt) with the weights
+        // of tile kt, written out as NS chunks that the compiler may not
+        // reorder across (sched_barrier): chunk i reads the K operand of
+        // MFMA i + PD - 1, issues MFMA i, takes the exponential of score i of
+        // tile kt and, as they complete, converts pairs of weights to 16 bits
+        // and adds groups of eight to the rounded-weight sum.  The vector
+        // instructions of a chunk then issue while its MFMA runs.
+        constexpr int NS = C::KK * C::NKB_;
+        constexpr int NSC = 16 * C::NKB_;            // scores per lane
+        constexpr int SPC = (NSC + NS - 1) / NS;      // scores per chunk
+        constexpr int NJ = C::NDMA_K + C::NDMA_V;
+        f32x16 sn[C::NKB_];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB_; ++kb) sn[kb] = f32x16{};
+        auto k_operand = [&](int i) __attribute__((always_inline)) {
+          const int kk = i / C::NKB_, kb = i % C::NKB_;
+          const int krow = kb * 32 + r32;
+          return *reinterpret_cast<const v8*>(Kn + krow * (DQ * 2) +
+                                              (((2 * kk + hh) ^ swz_k<DQ>(krow)) << 4));
+        };
+        v8 pb[C::NKB_][2];
+        float rs = 0.f;
+        v8 kring[PD];
+#pragma unroll
+        for (int i = 0; i < PD - 1; ++i) kring[i] = k_operand(i);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          if (i + PD - 1 < NS) kring[(i + PD - 1) % PD] = k_operand(i + PD - 1);
+          asm volatile("" ::: "memory");
+          sn[i % C::NKB_] = E::mfma(kring[i % PD], qf[i / C::NKB_], sn[i % C::NKB_]);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            if ((j * NS) / NJ == i) issue_one(j);
+#pragma unroll
+          for (int u = 0; u < SPC; ++u) {
+            const int sidx = i * SPC + u;
+            if (sidx < NSC) {
+              const int kb = sidx / 16, v = sidx % 16;
+              const float pw = exp2_fast(__builtin_fmaf(sc[kb][v], c, -m_use));
+              sc[kb][v] = pw;
+              rs += pw;
+              if (v & 1) {
+                pb[kb][v >> 3][(v & 7) - 1] = (T)sc[kb][v - 1];
+                pb[kb][v >> 3][v & 7] = (T)pw;
+              }
+              if ((v & 7) == 7) lh_run = E::sum8(pb[kb][v >> 3], lh_run);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run += rs;
+
+        // P.V of tile kt; rows that see at most one tile of keys also add
+        // the rounding remainder of P (as in the loop above)
+        if (kbase < C::BN && lim_w <= C::BN) {
+          keep_branch();
+          v8 pl[C::NKB_][2];
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                pl[kb][a2][j] = (T)(sc[kb][8 * a2 + j] - (float)pb[kb][a2][j]);
+#pragma unroll
+          for (int kb = 0; kb < C::NKB_; ++kb)
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2) lh_run = E::sum8(pl[kb][a2], lh_run);
+          pv_tile(Vs, pl, [](int) {});
+        }
+        // P.V of tile kt with the row max of tile kt + 1 (one score per
+        // product); then the rescale, if any, before the weights of kt + 1
+        mask_tile(sn, kbase + C::BN);
+        float mx = -INFINITY;
+        pv_tile(Vs, pb, [&](int i) __attribute__((always_inline)) {
+          constexpr int NSC = 16 * C::NKB_;
+          constexpr int NPV = C::DB * C::NKB_ * 2;
+          constexpr int SPP = (NSC + NPV - 1) / NPV;
+#pragma unroll
+          for (int u = 0; u < SPP; ++u)
+            if (i * SPP + u < NSC) mx = fmaxf(mx, sn[(i * SPP + u) / 16][(i * SPP + u) % 16]);
+        });
+        m_use = settle_max(mx, kt + 1 < kt_end);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB_; ++kb) sc[kb] = sn[kb];
+      }
     } else {
-      // one workgroup per CU (d = 256): the unrolled form's extra registers
-      // cost more than the address arithmetic it saves
+      // key-range form with one workgroup per CU: the plain loop
       for (int kt = kt_begin; kt < kt_end; ++kt) tile_step(kt, (kt - kt_begin) & 1);
     }
 
