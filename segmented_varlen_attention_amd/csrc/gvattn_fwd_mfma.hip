@@ -690,7 +690,10 @@ void fwd_mfma_kernel(FwdArgs a) {
         // MFMA i + PD - 1, issues MFMA i, takes the exponential of score i of
         // tile kt and, as they complete, converts pairs of weights to 16 bits
         // and adds groups of eight to the rounded-weight sum.  The vector
-        // instructions of a chunk then issue while its MFMA runs.
+        // instructions of a chunk then issue while its MFMA runs.  The loads
+        // of step kt go out over the first half of the chunks: the P.V reads
+        // below wait for them (the transposed-read builtin carries no alias
+        // information, so the compiler waits for every LDS-DMA in flight).
         constexpr int NS = C::KK * C::NKB_;
         constexpr int NSC = 16 * C::NKB_;            // scores per lane
         constexpr int SPC = (NSC + NS - 1) / NS;      // scores per chunk
@@ -716,7 +719,7 @@ void fwd_mfma_kernel(FwdArgs a) {
           sn[i % C::NKB_] = E::mfma(kring[i % PD], qf[i / C::NKB_], sn[i % C::NKB_]);
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            if ((j * NS) / NJ == i) issue_one(j);
+            if ((j * ((NS + 1) / 2)) / NJ == i) issue_one(j);
 #pragma unroll
           for (int u = 0; u < SPC; ++u) {
             const int sidx = i * SPC + u;
