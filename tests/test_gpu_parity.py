@@ -111,7 +111,7 @@ def test_many_segments_tiny_lengths(nseg):
 
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_score_jumps_across_key_tiles(dtype, d, causal):
     """Key tiles whose scores are 32x larger (or smaller) than the previous
@@ -134,6 +134,31 @@ def test_score_jumps_across_key_tiles(dtype, d, causal):
     out, lse, _ = DeviceCase(wl).fwd()
     say(f"[score jumps {dtype} d{d} c{int(causal)}]",
         compare_full(out, lse, wl, where=f"score jumps {dtype} d{d} c{int(causal)}", derived=True))
+
+
+@pytest.mark.parametrize("d,dv", [(256, 256), (128, 256), (256, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_jumps_long_keys_large_heads(d, dv, causal):
+    """The large-head kernels take a tile's row max, and raise the running
+    max and rescale O, after the previous tile's P.V and before the tile's
+    own weights.  Eleven 64-key tiles whose key scale jumps by up to 32x
+    every 32 keys (growth and decay of the row max in the middle of the key
+    sequence, several times per row), in bf16 against the oracle."""
+    seed = 1300 + d + dv + 7 * causal
+    uq, uk = [96, 64, 33], [700, 690, 650]
+    wl = W.random_small(seed, 3, 96, 700, 8, 2, d, causal, W.BF16, lengths=(uq, uk), dv=dv)
+    g = wl.geom
+    factors = np.array([0.25, 8.0, 0.25, 1.0, 8.0, 0.5, 0.25, 8.0, 2.0, 0.125, 4.0])
+    k = wl.k.copy()
+    for seg in range(g.nseg):
+        k0 = int(g.cu_k[seg])
+        j = np.arange(int(g.cu_k[seg + 1]) - k0)
+        k[k0 + j] *= factors[(j // 32) % len(factors)][:, None, None]
+    wl.k = W.round_to(W.BF16, k)
+    out, lse, _ = DeviceCase(wl).fwd()
+    say(f"[score jumps, long keys, d{d} dv{dv} c{int(causal)}]",
+        compare_full(out, lse, wl, where=f"score jumps long d{d} dv{dv} c{int(causal)}",
+                     derived=True))
 
 
 # --- the five workloads -------------------------------------------------------------
