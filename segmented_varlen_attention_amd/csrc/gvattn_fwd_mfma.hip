@@ -539,16 +539,16 @@ void fwd_mfma_kernel(FwdArgs a) {
     } else if constexpr (!KR) {
       // One workgroup per CU (d > 128), so one wave per SIMD: no other wave
       // fills the matrix cores while this one runs its softmax.  The loop is
-      // software-pipelined instead, with K one tile ahead of V.  Step t takes
-      // the row max of tile t (and the rare rescale), then computes the
-      // scores of tile t + 1 in one straight-line block with the
-      // exponentials and 16-bit conversion of tile t, so that matrix-core
-      // and vector instructions interleave, then P.V of tile t.  K(t) and
-      // V(t) sit in stage (t - kt_begin) & 1 as in the loop above; step t
-      // loads K(t + 2) into the stage K(t) leaves and V(t + 1) into the one
-      // V(t - 1) left.  Past the last tile the loads go through zero-size
-      // resources (zeros into stages nobody reads), so the scores of the
-      // tile after the last one are computed, from zeros, and dropped.
+      // software-pipelined instead, with K one tile ahead of V.  Step t
+      // computes the scores of tile t + 1 interleaved with the exponentials
+      // and 16-bit conversion of tile t, then P.V of tile t interleaved with
+      // the row max of tile t + 1, then (rarely) raises the running max and
+      // rescales O before the weights of tile t + 1.  K(t) and V(t) sit in
+      // stage (t - kt_begin) & 1 as in the loop above; step t loads K(t + 2)
+      // into the stage K(t) leaves and V(t + 1) into the one V(t - 1) left.
+      // Past the last tile the loads go through zero-size resources (zeros
+      // into stages nobody reads), so the scores of the tile after the last
+      // one are computed, from zeros, and dropped.
       auto stage_of = [&](int kt) __attribute__((always_inline)) {
         return lds + ((kt - kt_begin) & 1) * C::STAGE_BYTES;
       };
@@ -559,9 +559,9 @@ void fwd_mfma_kernel(FwdArgs a) {
                                                    (((2 * kk + hh) ^ swz_k<DQ>(krow)) << 4));
         sv[kb] = E::mfma(ka, qf[kk], sv[kb]);
       };
-      // P.V with the V^T operands read PD products ahead (one wave per SIMD:
-      // no other wave hides the LDS latency), consecutive products
-      // accumulating into different O blocks
+      // P.V with each V^T operand read PD - 1 products ahead of its use (one
+      // wave per SIMD: no other wave hides the LDS latency), consecutive
+      // products accumulating into different O blocks
       constexpr int PD = 3;
       auto pv_tile = [&](const char* Vs, const v8 (&p)[C::NKB_][2], auto&& work)
                          __attribute__((always_inline)) {
