@@ -19,12 +19,14 @@
 // result does not depend on the order, so outputs are deterministic.
 // Segment lengths, splits and offsets stay in LDS for launches of up to
 // kPlanLdsSegs segments (the tile loops then read no global memory), and the
-// prefix sums are wave shuffles plus one exchange of wave totals (up to 64
-// segments or 512 buckets, one wave alone and no exchange).  The kernel is
+// prefix sums and reductions move values between the lanes of a wave with
+// DPP, in registers, plus one exchange of wave totals (up to 64 segments or
+// 512 buckets, one wave alone and no exchange).  The kernel is
 // latency-bound: one memory round trip, a few barriers and the LDS
 // atomics.  Each thread takes a contiguous run of entries (one segment
 // lookup for all of them), and the atomics of a wave are aggregated over
 // neighbouring lanes with equal keys.
+#include <climits>
 #include <type_traits>
 
 #include "gvattn_internal.h"
@@ -43,18 +45,64 @@ constexpr int kExactCost = 16;  // a multiple of 2^kGroupShift
 // a launch with more segments reads them from global memory instead.
 constexpr int kPlanLdsSegs = 2048;
 
+// Cross-lane steps on DPP (the data-parallel-primitive operand modifier of
+// gfx9 vector instructions), which move values between lanes in registers
+// instead of a round trip through the LDS crossbar (ds_bpermute):
+// row_shr:n reads the lane n below inside each row of 16 lanes, row_bcast:15
+// hands lane 15 of each row to the row above it, row_bcast:31 hands lane 31
+// to rows 2 and 3.  A lane whose source is outside its row, or whose row the
+// row mask leaves out, gets `id`.
+constexpr int kDppRowShr = 0x110;  // + n
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_int(int v, int id) {
+  return __builtin_amdgcn_update_dpp(id, v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ long long dpp_int(long long v, long long id) {
+  const int lo = __builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(id >> 32), (int)(v >> 32), CTRL, ROWS, 0xf, false);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// Inclusive scan of op over the 64 lanes of a wave (every lane takes part):
+// shifts of 1, 2, 4 and 8 lanes inside each row, then every row combines
+// the totals of the rows below it.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_inclusive(T v, T id, Op op) {
+  v = op(v, dpp_int<kDppRowShr + 1, 0xf>(v, id));
+  v = op(v, dpp_int<kDppRowShr + 2, 0xf>(v, id));
+  v = op(v, dpp_int<kDppRowShr + 4, 0xf>(v, id));
+  v = op(v, dpp_int<kDppRowShr + 8, 0xf>(v, id));
+  v = op(v, dpp_int<kDppRowBcast15, 0xa>(v, id));
+  v = op(v, dpp_int<kDppRowBcast31, 0xc>(v, id));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T lane63(T v) {
+  if constexpr (sizeof(T) == 8) {
+    const unsigned lo = __builtin_amdgcn_readlane((int)v, 63);
+    const unsigned hi = __builtin_amdgcn_readlane((int)((long long)v >> 32), 63);
+    return (T)(((unsigned long long)hi << 32) | lo);
+  } else {
+    return (T)__builtin_amdgcn_readlane((int)v, 63);
+  }
+}
+
+struct AddOp {
+  template <typename T> __device__ T operator()(T a, T b) const { return a + b; }
+};
+
 // Exclusive prefix sum over the workgroup: an inclusive scan inside each
-// wave (shuffles), then the wave totals from LDS.  *total gets the sum of
-// all x.  `wsum` holds kPlanWaves values.
+// wave, then the wave totals from LDS.  *total gets the sum of all x.
+// `wsum` holds kPlanWaves values.
 template <typename T>
 __device__ T block_exclusive_scan(T x, T* wsum, T* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  T v = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const T y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
+  const T v = wave_inclusive<T>(x, T(0), AddOp{});
   if (lane == 63) wsum[w] = v;
   __syncthreads();
   T base = 0, tot = 0;
@@ -69,29 +117,19 @@ __device__ T block_exclusive_scan(T x, T* wsum, T* total) {
   return base + v - x;
 }
 
-// Wave reductions (every lane of the wave takes part).
+// Wave reductions (every lane of the wave takes part; uniform result).
 __device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
-  return x;
+  return lane63(wave_inclusive<int>(x, INT_MIN, [](int a, int b) { return max(a, b); }));
 }
 __device__ __forceinline__ int wave_or(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x |= __shfl_xor(x, off, 64);
-  return x;
+  return lane63(wave_inclusive<int>(x, 0, [](int a, int b) { return a | b; }));
 }
 
 // Exclusive prefix sum over the 64 lanes of one wave; *total gets the sum.
 template <typename T>
 __device__ __forceinline__ T wave_exclusive_scan(T x, T* total) {
-  const int lane = threadIdx.x & 63;
-  T v = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const T y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
-  *total = __shfl(v, 63, 64);
+  const T v = wave_inclusive<T>(x, T(0), AddOp{});
+  *total = lane63(v);
   return v - x;
 }
 
@@ -450,7 +488,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       int4 e = make_int4(0, 0, 0, 0);
       int key = 0;
       if (on) {
-        while (t >= e1) {  // segments without entries are passed over
+        while (t >= e1 && s + 1 < nseg) {  // segments without entries are passed over
           ++s;
           e0 = e1;
           e1 = v.off[s + 1];
@@ -526,15 +564,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   __syncthreads();
 
-  // 4. scatter (the header below takes nothing from it: no barrier)
+  // 4. scatter (the header below takes nothing from it: no barrier).  The
+  // positions are below n_tiles by construction; the checks keep every
+  // store inside the list whatever the counts.
   if (cached) {  // hist holds the bucket starts now
 #pragma unroll
     for (int i = 0; i < kCached; ++i)
-      if (c_on[i]) a.ws.tiles[hist[c_key[i]] + c_rank[i]] = c_ent[i];
+      if (c_on[i]) {
+        const int pos = hist[c_key[i]] + c_rank[i];
+        if ((unsigned)pos < (unsigned)n_tiles) a.ws.tiles[pos] = c_ent[i];
+      }
   } else {
     walk(std::integral_constant<int, 0>{}, [&](int, const int4& e, int key, bool on) {
       const int pos = wave_reserve(hist, key, on);
-      if (on) a.ws.tiles[pos] = e;
+      if (on && (unsigned)pos < (unsigned)n_tiles) a.ws.tiles[pos] = e;
     });
   }
 
