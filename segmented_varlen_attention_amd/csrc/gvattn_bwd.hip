@@ -688,30 +688,48 @@ __global__ __launch_bounds__(256, 3) void bwd_dkv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK / dV of split items: sum of the chunks' FP32 partials
 // ---------------------------------------------------------------------------
+// A block takes one slab of kRedRows key rows of a split item; each of its
+// threads issues the loads of all S partials of a 16-byte column before
+// adding them, in chunk order, so that the loads of one column are in
+// flight together instead of one after another.
+constexpr int kRedRows = 16;
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a) {
   const PlanHeader* hdr = a.kws.header;
-  if (hdr->key != a.kkey) return;  // the dK / dV kernel reported it
+  // a plan of another geometry: the dK / dV kernel reported it; no split
+  // item: nothing to reduce
+  if (hdr->key != a.kkey || hdr->max_split <= 1) return;
   const int hkv = a.g.hkv;
   const int n_work = hdr->n_tiles * hkv;
   constexpr int W = D + DV;
   constexpr int C4 = W / 4;  // float4 columns per key row
-  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+  constexpr int NSLAB = kBwdKeyRows / kRedRows;
+  const int64_t jstride = (int64_t)hkv * kBwdKeyRows * C4;  // between chunks, in float4
+  for (int v = blockIdx.x; v < n_work * NSLAB; v += gridDim.x) {
+    const int w = v / NSLAB, slab = v - w * NSLAB;
     const int t = w / hkv, kvh = w - t * hkv;
     const int4 tile = a.kws.tiles[t];
     // chunk 0 of a split item reduces it; its slot is the first of S
     if (!(tile.w & 1) || ((tile.w >> 1) & 15) != 0) continue;
     const int seg = tile.x, k_row0 = tile.y;
     const int slot0 = (int)((uint32_t)tile.w >> 5);
-    const int S = a.kws.seg_split[seg];
+    const int S = max(1, min(a.kws.seg_split[seg], kMaxSplits));
     const int k0 = a.g.cu_k[seg], uk = a.g.used_k[seg];
-    for (int i = threadIdx.x; i < kBwdKeyRows * C4; i += blockDim.x) {
-      const int kr = i / C4, c4 = i - kr * C4;
+    const f32x4* part = reinterpret_cast<const f32x4*>(a.kpart) +
+                        ((int64_t)slot0 * hkv + kvh) * kBwdKeyRows * C4;
+    for (int i = threadIdx.x; i < kRedRows * C4; i += blockDim.x) {
+      const int kr = slab * kRedRows + i / C4, c4 = i % C4;
       if (k_row0 + kr >= uk) continue;
+      const f32x4* p = part + kr * C4 + c4;
+      // every load unconditional (chunks past S read chunk S - 1 again), so
+      // that they form one block and issue back to back
+      f32x4 pj[kMaxSplits];
+#pragma unroll
+      for (int j = 0; j < kMaxSplits; ++j) pj[j] = p[min(j, S - 1) * jstride];
       f32x4 sum = f32x4{};
-      for (int j = 0; j < S; ++j)
-        sum += *reinterpret_cast<const f32x4*>(
-            a.kpart + (((int64_t)(slot0 + j) * hkv + kvh) * kBwdKeyRows + kr) * W + 4 * c4);
+#pragma unroll
+      for (int j = 0; j < kMaxSplits; ++j)
+        if (j < S) sum += pj[j];
       const int64_t row = (int64_t)(k0 + k_row0 + kr) * hkv + kvh;
       typename Elem<T>::v4 o;
       if (4 * c4 < D) {
