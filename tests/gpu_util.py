@@ -284,3 +284,33 @@ def compare_sampled(out, lse, wl, samples, geom=None, where=""):
         stats.append(compare(o_gpu, l_gpu, o_ref, l_ref, g.dtype,
                              f"{where} seg {seg}"))
     return merge_stats(stats)
+
+
+# (d, d_v) pairs the forward supports, and those of the backward
+DIMS_FWD = [(a, b) for a in (64, 128, 256) for b in (64, 128, 256)]
+DIMS_BWD = [(a, b) for a in (64, 128) for b in (64, 128)]
+
+
+def random_geometry(seed, dims, dtypes, cap=300):
+    """Everything drawn from one seed: 1-11 segments whose query and key
+    capacities are independent in [0, cap] (gaps of any size, empty
+    segments), used lengths uniform in [0, capacity], G in 1..4 with 1 or 2
+    KV heads, a (d, d_v) pair from ``dims``, a dtype from ``dtypes``, causal
+    or not, and an input spread of 0.5, 1 or 2 (softmax from flat to
+    sharp).  Returns the workload and the spread."""
+    rng = np.random.default_rng(seed)
+    nseg = int(rng.integers(1, 11, endpoint=True))
+    cap_q = rng.integers(0, cap, size=nseg, endpoint=True)
+    cap_k = rng.integers(0, cap, size=nseg, endpoint=True)
+    uq = [int(rng.integers(0, c, endpoint=True)) for c in cap_q]
+    uk = [int(rng.integers(0, c, endpoint=True)) for c in cap_k]
+    hkv = int(rng.integers(1, 2, endpoint=True))
+    g = int(rng.integers(1, 4, endpoint=True))
+    d, dv = dims[int(rng.integers(len(dims)))]
+    dtype = dtypes[int(rng.integers(len(dtypes)))]
+    causal = bool(rng.integers(2))
+    std = (0.5, 1.0, 2.0)[int(rng.integers(3))]
+    geom = W.make_geometry(list(cap_q), list(cap_k), uq, uk, g * hkv, hkv, d, causal,
+                           dtype=dtype, dv=dv)
+    q, k, v = W.fill_qkv(geom, seed + 1000, std=std)
+    return W.Workload(f"random_s{seed}", seed, geom, q, k, v), std

@@ -23,7 +23,7 @@ import oracle
 from segmented_varlen_attention_amd import binding as B
 from segmented_varlen_attention_amd import workloads as W
 
-from gpu_util import i32, say, to_np, torch, upload
+from gpu_util import DIMS_BWD, i32, random_geometry, say, to_np, torch, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +140,19 @@ def test_bwd_random(dtype, d, dv, causal):
     uq[2], uk[2] = 0, 45      # keys without rows
     wl = W.random_small(seed, nseg, 160, 300, 8, 2, d, causal, dtype, lengths=(uq, uk), dv=dv)
     check_case(wl, seed, f"bwd {dtype} d{d} dv{dv} c{int(causal)}")
+
+
+@pytest.mark.parametrize("seed", range(960, 972))
+def test_bwd_random_geometries(seed):
+    """Seeded random geometries: segment counts, independent query and key
+    capacities (gaps, empty segments), GQA layouts, head dims, bf16 / fp16,
+    causal or not, input spreads 0.5-2; every gradient element against the
+    oracle."""
+    wl, std = random_geometry(seed, DIMS_BWD, (W.BF16, W.FP16))
+    g = wl.geom
+    say(f"[bwd random] seed={seed} {g.dtype} d={g.d} dv={g.dv} hq={g.hq} hkv={g.hkv} "
+        f"causal={g.causal} std={std} uq={g.used_q.tolist()} uk={g.used_k.tolist()}")
+    check_case(wl, seed, f"bwd random seed {seed}")
 
 
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (12, 4), (8, 1)])

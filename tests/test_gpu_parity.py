@@ -13,8 +13,9 @@ import oracle
 from segmented_varlen_attention_amd import binding as B
 from segmented_varlen_attention_amd import workloads as W
 
-from gpu_util import (DeviceCase, check_gap_rows, compare, compare_full, compare_sampled, i32,
-                      oracle_abs, say, tile_rows, to_np, torch, used_row_mask)
+from gpu_util import (DIMS_FWD, DeviceCase, check_gap_rows, compare, compare_full,
+                      compare_sampled, i32, oracle_abs, random_geometry, say, tile_rows, to_np,
+                      torch, used_row_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,36 +95,9 @@ def test_small_fp32(d, causal):
 
 # --- seeded random geometries: every used row -----------------------------------
 
-DIM_PAIRS = [(a, b) for a in (64, 128, 256) for b in (64, 128, 256)]
-
-
-def random_geometry(seed):
-    """Everything drawn from one seed: 1-11 segments whose query and key
-    capacities are independent in [0, 300] (gaps of any size, empty
-    segments), used lengths uniform in [0, capacity], G in 1..4 with 1 or 2
-    KV heads, any supported (d, d_v) pair, bf16 / fp16 / fp32, causal or not,
-    and an input spread of 0.5, 1 or 2 (softmax from flat to sharp)."""
-    rng = np.random.default_rng(seed)
-    nseg = int(rng.integers(1, 11, endpoint=True))
-    cap_q = rng.integers(0, 300, size=nseg, endpoint=True)
-    cap_k = rng.integers(0, 300, size=nseg, endpoint=True)
-    uq = [int(rng.integers(0, c, endpoint=True)) for c in cap_q]
-    uk = [int(rng.integers(0, c, endpoint=True)) for c in cap_k]
-    hkv = int(rng.integers(1, 2, endpoint=True))
-    g = int(rng.integers(1, 4, endpoint=True))
-    d, dv = DIM_PAIRS[int(rng.integers(len(DIM_PAIRS)))]
-    dtype = (W.BF16, W.FP16, W.FP32)[int(rng.integers(3))]
-    causal = bool(rng.integers(2))
-    std = (0.5, 1.0, 2.0)[int(rng.integers(3))]
-    geom = W.make_geometry(list(cap_q), list(cap_k), uq, uk, g * hkv, hkv, d, causal,
-                           dtype=dtype, dv=dv)
-    q, k, v = W.fill_qkv(geom, seed + 1000, std=std)
-    return W.Workload(f"random_s{seed}", seed, geom, q, k, v), std
-
-
 @pytest.mark.parametrize("seed", range(900, 924))
 def test_random_geometries(seed):
-    wl, std = random_geometry(seed)
+    wl, std = random_geometry(seed, DIMS_FWD, (W.BF16, W.FP16, W.FP32))
     g = wl.geom
     say(f"[random] seed={seed} {g.dtype} d={g.d} dv={g.dv} hq={g.hq} hkv={g.hkv} "
         f"causal={g.causal} std={std} caps_q={np.diff(g.cu_q).tolist()} uq={g.used_q.tolist()} "
