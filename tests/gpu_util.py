@@ -314,3 +314,27 @@ def random_geometry(seed, dims, dtypes, cap=300):
                            dtype=dtype, dv=dv)
     q, k, v = W.fill_qkv(geom, seed + 1000, std=std)
     return W.Workload(f"random_s{seed}", seed, geom, q, k, v), std
+
+
+def random_decode_geometry(seed, dims, dtypes):
+    """Decode-like draws from one seed: 1-24 segments with 0-12 used query
+    rows (capacity up to 4 more) and 0-6000 keys (capacity up to 64 more),
+    G in 1..4 with 1-4 KV heads, a (d, d_v) pair from ``dims``, a dtype from
+    ``dtypes``, causal or not: launches small enough for the plan to split
+    the key ranges."""
+    rng = np.random.default_rng(seed)
+    nseg = int(rng.integers(1, 24, endpoint=True))
+    uq = rng.integers(0, 12, size=nseg, endpoint=True)
+    uk = rng.integers(0, 6000, size=nseg, endpoint=True)
+    cap_q = uq + rng.integers(0, 4, size=nseg, endpoint=True)
+    cap_k = uk + rng.integers(0, 64, size=nseg, endpoint=True)
+    hkv = int(rng.integers(1, 4, endpoint=True))
+    g = int(rng.integers(1, 4, endpoint=True))
+    d, dv = dims[int(rng.integers(len(dims)))]
+    dtype = dtypes[int(rng.integers(len(dtypes)))]
+    causal = bool(rng.integers(2))
+    geom = W.make_geometry(list(cap_q), list(cap_k), list(uq), list(uk), g * hkv, hkv, d, causal,
+                           dtype=dtype, dv=dv)
+    q, k, v = W.fill_qkv(geom, seed + 1000)
+    return W.Workload(f"random_decode_s{seed}", seed, geom, q, k, v)
+

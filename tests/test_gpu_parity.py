@@ -14,8 +14,8 @@ from segmented_varlen_attention_amd import binding as B
 from segmented_varlen_attention_amd import workloads as W
 
 from gpu_util import (DIMS_FWD, DeviceCase, check_gap_rows, compare, compare_full,
-                      compare_sampled, i32, oracle_abs, random_geometry, say, tile_rows, to_np,
-                      torch, used_row_mask)
+                      compare_sampled, i32, oracle_abs, random_decode_geometry, random_geometry,
+                      say, tile_rows, to_np, torch, used_row_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -528,6 +528,26 @@ def test_split_k_decode(dtype, d, dv, causal):
     st = compare_full(out, lse, wl, where=f"split {dtype} d{d} dv{dv} c{int(causal)}",
                       derived=True)
     say(f"[split-K] {dtype} d={d} dv={dv} causal={causal} max split {max_split(ws)}", st)
+    out2, lse2, _ = dc.fwd(fn=B.gvattn_fwd_run, workspace=ws)
+    t = torch()
+    assert t.equal(out.view(t.int16), out2.view(t.int16))
+    assert t.equal(lse.view(t.int32), lse2.view(t.int32))
+
+
+@pytest.mark.parametrize("seed", range(700, 712))
+def test_split_k_random_decode(seed):
+    """Seeded decode-like launches (few query rows, up to 6000 keys, random
+    GQA layout, head dims, dtype and mask): every used row against the
+    oracle, and the same plan run twice gives bit-identical results."""
+    wl = random_decode_geometry(seed, DIMS_FWD, (W.BF16, W.FP16))
+    g = wl.geom
+    dc = DeviceCase(wl)
+    out, lse, ws = dc.fwd()
+    assert B.gvattn_read_device_error(ws) == 0
+    say(f"[split-K random] seed={seed} {g.dtype} d={g.d} dv={g.dv} hq={g.hq} hkv={g.hkv} "
+        f"causal={g.causal} uq={g.used_q.tolist()} max split {max_split(ws)}")
+    st = compare_full(out, lse, wl, where=f"split random seed {seed}", derived=True)
+    say("   ", st)
     out2, lse2, _ = dc.fwd(fn=B.gvattn_fwd_run, workspace=ws)
     t = torch()
     assert t.equal(out.view(t.int16), out2.view(t.int16))
