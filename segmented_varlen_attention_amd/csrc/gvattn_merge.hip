@@ -26,7 +26,6 @@ namespace {
 using namespace dev;
 
 constexpr int kThreads = 256;
-constexpr int kElems = 32;  // split merge: elements of one (row, head) per lane
 // LSE merge: elements of one (row, head) per lane, held in runs of 8 spread
 // over the row so that each 16-byte load instruction of the D/kMergeElems
 // lanes of a pair reads one contiguous piece of it
@@ -266,70 +265,91 @@ hipError_t launch_t(const MergeArgs& a, hipStream_t s, bool* ok) {
   }
 }
 
-// Split-K merge: for every used row of a segment the plan split into S > 1
-// key chunks, combine the chunks' FP32 partials (O over the chunk, LSE of
-// the chunk) exactly as the LSE merge combines partitions, into out / lse.
+// Split-K merge over the plan's entries.  A block takes RPB rows of one
+// head of a split query tile (the entry of the tile's chunk 0) and combines
+// the chunks' FP32 partials of those rows (O over the chunk, LSE of the
+// chunk) as the LSE merge combines partitions.  The entry names the rows,
+// so there is no segment lookup and no gap row.  Each lane holds 8
+// elements of a row; the loads of all chunks go out together (every chunk's
+// LSE at once, the partial rows four chunks at a time; chunks past S read
+// chunk S - 1 again and are left out) and the sums run in chunk order.
 template <typename TOut, int D>
 __global__ __launch_bounds__(kThreads) void split_merge_kernel(FwdArgs a) {
-  constexpr int LPP = D / kElems;
-  constexpr int PPB = kThreads / LPP;
+  constexpr int LPR = D / 8;           // lanes per row
+  constexpr int RPB = kThreads / LPR;  // rows per block
   const PlanHeader* hdr = a.ws.header;
   if (hdr->key != a.key || hdr->n_tiles == 0 || hdr->max_split <= 1) return;
-  const int sub = threadIdx.x % LPP;
-  const int slot = threadIdx.x / LPP;
   const int hq = a.g.hq, total_q = a.g.total_q;
-  const int64_t npairs = (int64_t)hq * total_q;
-  const int64_t first = (int64_t)blockIdx.x * PPB;
-  if (first + slot >= npairs) return;
-  const int64_t row_first = first / hq;
-  const int t = (int)(first - row_first * hq) + slot;
-  const int row = (int)(row_first + t / hq);
-  const int head = t % hq;
-  const int s = find_segment(a.g.cu_q, a.g.nseg, row);
-  const int S = a.ws.seg_split[s];
-  if (S <= 1) return;
-  const int c0 = a.g.cu_q[s], us = a.g.used_q[s];
-  if (row < c0 || row >= c0 + us) return;
+  const int rows = hdr->rows_per_tile;
+  const int nsub = (rows + RPB - 1) / RPB;
+  const int64_t n_units = (int64_t)hdr->n_tiles * hq * nsub;
+  const int lr = threadIdx.x / LPR, c = (threadIdx.x % LPR) * 8;
+  for (int64_t v = blockIdx.x; v < n_units; v += gridDim.x) {
+    const int sub = (int)(v % nsub);
+    const int64_t th = v / nsub;
+    const int head = (int)(th % hq);
+    const int t = (int)(th / hq);
+    const int4 tile = a.ws.tiles[t];
+    if (!(tile.w & 1) || ((tile.w >> 1) & 15) != 0) continue;  // chunk 0 of a split tile
+    const int seg = tile.x;
+    const int rl = sub * RPB + lr;  // row within the tile
+    const int r = tile.y + rl;      // row within the segment
+    if (rl >= rows || r >= a.g.used_q[seg]) continue;
+    const int S = max(1, min(a.ws.seg_split[seg], kMaxSplits));
+    const int64_t grow = (int64_t)a.g.cu_q[seg] + r;
 
-  float m = -INFINITY;
-  for (int j = 0; j < S; ++j)
-    m = fmaxf(m, a.ws.part_lse[((int64_t)j * hq + head) * total_q + row]);
-  float acc[kElems];
+    float L[kMaxSplits];
 #pragma unroll
-  for (int i = 0; i < kElems; ++i) acc[i] = 0.f;
-  float lse_out = -INFINITY;
-  if (m != -INFINITY) {
-    constexpr float kLog2e = 1.4426950408889634f;
-    float wsum = 0.f;
-    for (int j = 0; j < S; ++j) {
-      const float L = a.ws.part_lse[((int64_t)j * hq + head) * total_q + row];
-      const float w = __builtin_amdgcn_exp2f((L - m) * kLog2e);
-      const float* src = a.ws.part_o + (((int64_t)j * total_q + row) * hq + head) * D + sub * kElems;
-      LaneRaw<float, kElems, 8> r;
-      r.load(src);
-      float f[kElems];
-      r.unpack(f);
-      wsum += w;
+    for (int j = 0; j < kMaxSplits; ++j)
+      L[j] = a.ws.part_lse[((int64_t)min(j, S - 1) * hq + head) * total_q + grow];
+    float m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kElems; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
+    for (int j = 0; j < kMaxSplits; ++j)
+      if (j < S) m = fmaxf(m, L[j]);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    float lse_out = -INFINITY;
+    if (m != -INFINITY) {
+      constexpr float kLog2e = 1.4426950408889634f;
+      constexpr int kBatch = 4;
+      float wsum = 0.f;
+#pragma unroll
+      for (int j0 = 0; j0 < kMaxSplits; j0 += kBatch) {
+        if (j0 < S) {
+          LaneRaw<float, 8, 8> raw[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            raw[u].load(a.ws.part_o + (((int64_t)min(j0 + u, S - 1) * total_q + grow) * hq + head) * D + c);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            if (j0 + u < S) {
+              const float w = __builtin_amdgcn_exp2f((L[j0 + u] - m) * kLog2e);
+              float f[8];
+              raw[u].unpack(f);
+              wsum += w;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
+            }
+          }
+        }
+      }
+      const float inv = 1.f / wsum;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= inv;
+      lse_out = m + logf(wsum);
     }
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int i = 0; i < kElems; ++i) acc[i] *= inv;
-    lse_out = m + logf(wsum);
+    Vec8<TOut>::store(static_cast<TOut*>(a.out) + (grow * hq + head) * D + c, acc);
+    if (c == 0) a.lse[(int64_t)head * total_q + grow] = lse_out;
   }
-  store_runs<TOut, kElems, 8>(static_cast<TOut*>(a.out) + ((int64_t)row * hq + head) * D + sub * kElems,
-                              acc);
-  if (sub == 0) a.lse[(int64_t)head * total_q + row] = lse_out;
 }
 
 template <typename TOut>
 hipError_t launch_split_t(const FwdArgs& a, hipStream_t s) {
-  const int per_block = kThreads / (a.g.dv / kElems);
-  const int64_t blocks = ((int64_t)a.g.hq * a.g.total_q + per_block - 1) / per_block;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(kThreads);
+  // one unit per (entry, head, block of rows), counted on the device; the
+  // blocks stride over them (units of entries that are not a split tile's
+  // chunk 0 are passed over)
+  const dim3 grid(8192), block(kThreads);
   switch (a.g.dv) {
     case 64: return launch_kernel(split_merge_kernel<TOut, 64>, grid, block, s, a);
     case 128: return launch_kernel(split_merge_kernel<TOut, 128>, grid, block, s, a);
